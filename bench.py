@@ -1,0 +1,350 @@
+"""Benchmark of the gated delta rule decode path on one MI355X.
+
+One step = one ``gdn_decode_norm`` call over a batch of 64 sequences at the real
+head shape (NV=48 value heads over NK=16 key heads, D=128, fp32 state with a
+1.25x padded slot pitch, fused gated RMS norm, fp32 output): index and pair,
+stage the per-head inputs, read the state tile once, reduce, update and write it
+back once, normalise and gate.  Consecutive steps cycle through ``--pools``
+distinct state pools (default 48, one per GDN layer of the model), so the state
+streams from HBM as it does in a real decode token rather than staying in the
+256 MB Infinity Cache.  Inputs are resident in HBM before timing starts.
+
+Prints ONE JSON line.  ``value`` is state GB/s (2*B*NV*D*D*4 bytes per step /
+step time); ``roofline`` covers the decode kernel with its full algorithmic
+bytes (state + inputs + outputs) against the 8 TB/s HBM peak; ``cpu_baseline``
+times the CPU oracle on a bounded sample of the same workload.  ``extra`` holds
+the other workloads (binary16 state at B=256, the 4096-token sequence
+recurrence, the B=1 real-head token over 48 layers, the cache-resident B=64
+case).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector (packed FMA)
+PMC_FILE = os.path.join(ROOT, "profiles", "decode_norm_b64_pmc.json")
+KERNEL_SOURCES = ("gdn_decode.hip", "gdn_device.h", "gdn_launch.h")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "gated_deltanet_decode_delta_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def head_bytes(D: int, NV: int, NK: int, state_bytes: int, out_bytes: int, norm: bool) -> float:
+    """Algorithmic HBM bytes of one (sequence, value head) step: the state tile
+    read and written once, q and k of the key head (shared by NV/NK value
+    heads), v, alpha, beta, and (with the norm) z, plus the output vector."""
+    b = 2.0 * D * D * state_bytes
+    b += 2.0 * D * 4 * NK / NV
+    b += D * 4 + 8 + D * out_bytes
+    if norm:
+        b += D * 4
+    return b
+
+
+def _timed(fn, steps: int, warmup: int):
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fn(i)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps          # ms per call
+
+
+def run_main(g, steps: int, warmup: int, pools: int):
+    import torch
+    from gated_deltanet_decode_delta_amd import inputs
+
+    cfg = inputs.CONFIGS["batched"]
+    B, NK, NV, D, pitch = cfg["B"], cfg["NK"], cfg["NV"], cfg["D"], cfg["pitch"]
+    c = inputs.config_case("batched")
+    dev = "cuda:0"
+    log(f"[bench] main: B={B} NV={NV} NK={NK} D={D} pitch={pitch} pools={pools}")
+    st0 = torch.from_numpy(c.state).to(dev)
+    states = [st0.clone() for _ in range(pools)]
+    del st0
+    base = {n: torch.from_numpy(getattr(c, n)).to(dev) for n in ("q", "k", "v", "z", "alpha", "beta")}
+    # every pool gets its own input buffers (the base rows rotated by the pool
+    # index), so no layer re-reads another layer's inputs from cache
+    sets = [{n: torch.roll(t, p, dims=0).contiguous() for n, t in base.items()} for p in range(pools)]
+    del base
+    gn = torch.from_numpy(c.gn).to(dev)
+    outs = [torch.empty((B, NV * D), dtype=torch.float32, device=dev) for _ in range(pools)]
+
+    def step(i):
+        p = i % pools
+        s = sets[p]
+        g.gdn_decode_norm(states[p], s["q"], s["k"], s["v"], s["alpha"], s["beta"], s["z"], gn,
+                          c.eps, out=outs[p], num_k_heads=NK, num_v_heads=NV)
+
+    ms = _timed(step, steps, warmup)
+    ms_hot = _timed(lambda i: step(0), steps, warmup)
+    state_bytes = 2.0 * B * NV * D * D * 4
+    algo_bytes = B * NV * head_bytes(D, NV, NK, 4, 4, True)
+    torch.cuda.synchronize()
+    bad = any(not bool(torch.isfinite(o).all()) for o in outs[:2])
+    del states, sets, outs
+    torch.cuda.empty_cache()
+    return dict(B=B, NV=NV, NK=NK, D=D, pitch=pitch, pools=pools, ms=ms, ms_hot=ms_hot,
+                state_bytes=state_bytes, algo_bytes=algo_bytes, nonfinite=bad)
+
+
+def run_fp16(g, calls: int):
+    import torch
+    from gated_deltanet_decode_delta_amd import inputs
+
+    c = inputs.config_case("fp16_state")
+    B, NK, NV, D = c.B, c.NK, c.NV, c.D
+    dev = "cuda:0"
+    log(f"[bench] fp16 state: B={B}")
+    st32 = torch.from_numpy(c.state).to(dev)
+    st16 = g.gdn_state_f32_to_f16(st32)
+    del st32
+    t = {n: torch.from_numpy(getattr(c, n)).to(dev) for n in ("q", "k", "v", "z", "alpha", "beta", "gn")}
+    out = torch.empty((B, NV * D), dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        g.gdn_decode_f16state(st16, t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["z"], t["gn"],
+                              c.eps, out=out, num_k_heads=NK, num_v_heads=NV)
+
+    ms = _timed(step, calls, 5)
+    state_bytes = 2.0 * B * NV * D * D * 2
+    algo = B * NV * head_bytes(D, NV, NK, 2, 2, True)
+    del st16, t, out
+    torch.cuda.empty_cache()
+    return {"workload": "fp16 state decode, B=256, NV=48, NK=16, D=128, fused norm, bf16 out",
+            "ms_per_call": round(ms, 5), "state_GBps": round(state_bytes / ms / 1e6, 1),
+            "hbm_frac_algorithmic": round(algo / ms / 1e6 / HBM_PEAK_GBS, 4),
+            "tokens_per_s_batch": round(B / ms * 1e3, 1)}
+
+
+def run_seq(g, calls: int):
+    import torch
+    from gated_deltanet_decode_delta_amd import inputs
+
+    c = inputs.config_case("sequence")
+    B, T, NK, NV, D = c.B, c.T, c.NK, c.NV, c.D
+    dev = "cuda:0"
+    log(f"[bench] sequence: B={B} T={T}")
+    t = {n: torch.from_numpy(getattr(c, n)).to(dev) for n in ("q", "k", "v", "alpha", "beta")}
+    st = torch.from_numpy(c.state).to(dev)
+    out = torch.empty((B * T, NV * D), dtype=torch.float32, device=dev)
+
+    def step(i):
+        g.gdn_recurrence_seq(st, t["q"], t["k"], t["v"], t["alpha"], t["beta"], out=out, seq_len=T,
+                             num_k_heads=NK, num_v_heads=NV, head_dim=D)
+
+    ms = _timed(step, calls, 1)
+    flops = 7.0 * D * D * B * NV * T
+    byts = B * T * (2 * NK * D * 4 + NV * (D * 4 + 8 + D * 4)) + 2.0 * B * NV * D * D * 4
+    del t, st, out
+    torch.cuda.empty_cache()
+    return {"workload": "sequence recurrence, B=4, T=4096, NV=48, NK=16, D=128, raw o",
+            "ms_per_call": round(ms, 4), "tflops": round(flops / ms / 1e9, 2),
+            "valu_frac": round(flops / ms / 1e9 / FP32_VALU_PEAK_TFLOPS, 4),
+            "GBps": round(byts / ms / 1e6, 1), "tokens_per_s": round(B * T / ms * 1e3, 1)}
+
+
+def run_real_head(g, tokens: int):
+    import torch
+    from gated_deltanet_decode_delta_amd import inputs
+
+    B, NK, NV, D, L = 1, 16, 48, 128, 48
+    dev = "cuda:0"
+    log("[bench] real head: B=1, 48 layers")
+    layers = []
+    for l in range(L):
+        c = inputs.make_case(2000 + l, B=B, NK=NK, NV=NV, D=D)
+        d = {n: torch.from_numpy(getattr(c, n)).to(dev) for n in ("q", "k", "v", "z", "alpha", "beta", "gn")}
+        d["state"] = torch.from_numpy(c.state).to(dev)
+        d["out"] = torch.empty((1, NV * D), device=dev)
+        layers.append(d)
+
+    def token(i):
+        for d in layers:
+            g.gdn_decode_norm(d["state"], d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["z"],
+                              d["gn"], 1e-6, out=d["out"], num_k_heads=NK, num_v_heads=NV)
+
+    ms = _timed(token, tokens, 3)
+    graph_ms = None
+    try:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            token(0)
+        torch.cuda.current_stream().wait_stream(s)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            token(0)
+        graph_ms = _timed(lambda i: graph.replay(), tokens, 3)
+    except Exception as e:  # capture is an optional measurement
+        log(f"[bench] graph capture skipped: {e}")
+    state_bytes = 2.0 * L * NV * D * D * 4
+    del layers
+    torch.cuda.empty_cache()
+    res = {"workload": "real head B=1, 48 layer states per token, fused norm fp32",
+           "us_per_token": round(ms * 1e3, 2), "tokens_per_s": round(1e3 / ms, 1),
+           "state_GBps": round(state_bytes / ms / 1e6, 1)}
+    if graph_ms is not None:
+        res.update({"graph_us_per_token": round(graph_ms * 1e3, 2),
+                    "graph_state_GBps": round(state_bytes / graph_ms / 1e6, 1)})
+    return res
+
+
+def cpu_baseline(seconds: float):
+    """The oracle on a bounded sample of the main workload: whole B=64 calls,
+    (sequence, head) pairs fanned out over the host's threads (capped at 16)."""
+    import oracle
+    from gated_deltanet_decode_delta_amd import inputs
+
+    c = inputs.config_case("batched")
+    B, NK, NV, D = c.B, c.NK, c.NV, c.D
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    heads = [(b, h) for b in range(B) for h in range(NV)]
+    st = c.state.copy()
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.seq_head_threaded(st, c.q, c.k, c.v, c.alpha, c.beta, B=B, T=1, NK=NK, NV=NV, Dk=D,
+                                 Dv=D, z=c.z, gn=c.gn, eps=c.eps, heads=heads, threads=threads)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or calls >= 200:
+            break
+    state_bytes = 2.0 * B * NV * D * D * 4 * calls
+    return {"value": round(state_bytes / el / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{calls} full B=64 gdn_decode_norm calls (3072 heads each) in {el:.1f} s "
+                      f"on {threads} host threads; state GB/s by the same formula",
+            "tokens_per_s_batch": round(B * calls / el, 1)}
+
+
+def pmc_traffic(algo_bytes: float):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources."""
+    try:
+        with open(PMC_FILE) as f:
+            pmc = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if pmc.get("kernel_hash") != kernel_hash():
+        return None
+    return pmc.get("bytes_per_launch")
+
+
+def calibrate_and_profile(g, steps: int):
+    """Launch sequence for the counter runs: a plain device copy of a known size,
+    then the main step; rocprofv3 --pmc reports both per dispatch."""
+    import torch
+    n = 1 << 28
+    a = torch.empty(n, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"[bench] copy kernel: {n * 4} bytes read, {n * 4} bytes written per dispatch")
+    del a, b
+    run_main(g, steps, 2, 48)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--pools", type=int, default=48)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-extra", action="store_true", help="main workload only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--pmc-run", action="store_true",
+                    help="copy-kernel calibration + main step only (for rocprofv3 --pmc)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_deltanet_decode_delta_amd as g
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    g.lib()
+    if args.pmc_run:
+        calibrate_and_profile(g, args.steps)
+        return
+
+    m = run_main(g, args.steps, args.warmup, args.pools)
+    ms = m["ms"]
+    B = m["B"]
+    value = m["state_bytes"] / ms / 1e6
+    achieved = m["algo_bytes"] / ms / 1e6
+    extra = {"cache_resident_single_pool": {
+        "ms_per_call": round(m["ms_hot"], 5),
+        "state_GBps": round(m["state_bytes"] / m["ms_hot"] / 1e6, 1),
+        "note": "same pool every call: the 201 MB state can stay in the 256 MB Infinity Cache"}}
+    if not args.no_extra:
+        extra["fp16_state"] = run_fp16(g, 100)
+        extra["sequence"] = run_seq(g, 3)
+        extra["real_head"] = run_real_head(g, 50)
+    cpu = None if args.no_cpu else cpu_baseline(args.cpu_seconds)
+    line = {
+        "metric": "GDN decode state GB/s and % HBM roofline; tokens/s·batch at HV=48,D=128",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "batched decode with fused gated RMSNorm: B=64, NV=48, NK=16, "
+                               "D=128, fp32 state pitch 1.25x slot, fp32 out, "
+                               f"{m['pools']} state pools in rotation",
+                   "global_batch": B, "seq_len": 1, "parallelism": "single GPU"},
+        "tokens_per_s_batch": round(B / ms * 1e3, 1),
+        "hbm_frac_state": round(value / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": pmc_traffic(m["algo_bytes"]),
+                     "kernel": "gdn::decode_kernel<128, float, kOutNormF32>",
+                     "algorithmic_bytes_per_launch": int(m["algo_bytes"])},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    if m["nonfinite"]:
+        line["warning"] = "non-finite outputs"
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

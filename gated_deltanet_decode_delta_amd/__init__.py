@@ -1,1 +1,300 @@
-"""Gated DeltaNet decode on MI355X (placeholder, binding follows)."""
+"""Gated DeltaNet (gated delta rule) state recurrence on AMD Instinct MI355X.
+
+A thin ctypes binding over ``libgdn.so`` (C ABI in ``include/gdn.h``).  The
+functions carry the C names and do argument marshalling only: they read
+pointers, element strides and the current HIP stream off torch tensors and call
+the library, which runs every step of the path in its own gfx950 kernels.  There
+is no fallback: if ``libgdn.so`` is missing or fails to load, every call raises.
+
+Tensor conventions (all fp32 CUDA tensors unless noted, inner dim contiguous):
+
+* ``state``: ``[B, pitch]`` or ``[B, NV, D, D]``; the row stride is the slot
+  pitch in elements.  ``gdn_decode_f16state`` takes a ``torch.float16`` pool.
+* ``q``, ``k``: ``[rows, >= NK*D]``; ``v``, ``z``: ``[rows, >= NV*D]``;
+  ``alpha``, ``beta``: ``[rows, >= NV]`` -- ``rows = B`` for decode and
+  ``B*T`` for the sequence (``[B, T, ...]`` is accepted and viewed as rows).
+  Row strides may exceed the width (views into a packed projection row).
+* ``norm_weight``: ``[D]``.  Outputs are ``[rows, NV*D]`` (allocated when not
+  given), fp32 or bf16.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgdn.so")
+
+GDN_OK = 0
+GDN_F32 = 0
+GDN_BF16 = 1
+STATUS_NAMES = {
+    0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_STRIDE",
+    4: "GDN_ERR_UNSUPPORTED", 5: "GDN_ERR_ALIAS", 6: "GDN_ERR_DTYPE", 7: "GDN_ERR_HIP",
+    8: "GDN_ERR_ARG",
+}
+EXPORTS = ("gdn_decode", "gdn_decode_norm", "gdn_decode_f16state", "gdn_recurrence_seq",
+           "gdn_state_f32_to_f16", "gdn_state_f16_to_f32", "gdn_status_string",
+           "gdn_last_hip_error")
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        msg = _lib().gdn_status_string(status).decode()
+        if status == 7:
+            msg += f" (hipError_t {_lib().gdn_last_hip_error()})"
+        super().__init__(f"{what}: {msg}")
+
+
+_LIB = None
+
+
+def _lib():
+    """Load ``libgdn.so`` (once) and declare the C signatures."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                           "(hipcc --offload-arch=gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, i32, f32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
+    lib.gdn_decode.argtypes = [vp, i64, vp, vp, i64, vp, i64, vp, vp, i64, vp, i64,
+                               i32, i32, i32, i32, i32, vp]
+    norm_sig = [vp, i64, vp, vp, i64, vp, i64, vp, vp, i64, vp, i64, vp, f32, vp, i32, i64,
+                i32, i32, i32, i32, i32, vp]
+    lib.gdn_decode_norm.argtypes = norm_sig
+    lib.gdn_decode_f16state.argtypes = norm_sig
+    lib.gdn_recurrence_seq.argtypes = [vp, i64, vp, vp, i64, vp, i64, vp, vp, i64, vp, i64, vp,
+                                       f32, vp, i64, i32, i32, i32, i32, i32, i32, vp]
+    lib.gdn_state_f32_to_f16.argtypes = [vp, vp, i64, vp]
+    lib.gdn_state_f16_to_f32.argtypes = [vp, vp, i64, vp]
+    for name in ("gdn_decode", "gdn_decode_norm", "gdn_decode_f16state", "gdn_recurrence_seq",
+                 "gdn_state_f32_to_f16", "gdn_state_f16_to_f32"):
+        getattr(lib, name).restype = ctypes.c_int
+    lib.gdn_status_string.argtypes = [ctypes.c_int]
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_last_hip_error.argtypes = []
+    lib.gdn_last_hip_error.restype = i32
+    _LIB = lib
+    return lib
+
+
+def lib():
+    """The raw ctypes handle of ``libgdn.so`` (signatures declared)."""
+    return _lib()
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(t, stream):
+    if stream is not None:
+        return int(stream)
+    return int(_torch().cuda.current_stream(t.device).cuda_stream)
+
+
+def _rows(t, rows: int, width: int, name: str, dtype=None):
+    """(pointer, row stride in elements) of a ``[rows, >= width]`` row array."""
+    torch = _torch()
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dim() > 2:
+        if t.shape[-1] < 1:
+            raise ValueError(f"{name} is empty")
+        try:
+            t = t.view(rows, -1)
+        except RuntimeError as e:
+            raise ValueError(f"{name} cannot be viewed as {rows} rows: {e}") from None
+    if t.dim() == 1:
+        t = t.view(1, -1)
+    if t.shape[0] != rows:
+        raise ValueError(f"{name}: expected {rows} rows, got {t.shape[0]}")
+    if t.shape[1] < width:
+        raise ValueError(f"{name}: rows of {t.shape[1]} < {width} elements")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name}: inner dimension must be contiguous")
+    stride = t.stride(0) if rows > 1 else max(t.shape[1], width)
+    return t.data_ptr(), int(stride), t
+
+
+def _state(state, batch: int, slot: int, dtype):
+    ptr, pitch, _ = _rows(state if state.dim() <= 2 else state.view(state.shape[0], -1),
+                          batch, slot, "state", dtype)
+    return ptr, pitch
+
+
+def _check(status: int, what: str):
+    if status != GDN_OK:
+        raise GdnError(status, what)
+
+
+def _dims(gn_or_none, num_k_heads, num_v_heads, head_dim):
+    if head_dim is None:
+        if gn_or_none is None:
+            raise ValueError("head_dim is required")
+        head_dim = gn_or_none.shape[0]
+    return int(num_k_heads), int(num_v_heads), int(head_dim)
+
+
+def _empty_rows(rows: int, width: int, dtype, like):
+    return _torch().empty((rows, width), dtype=dtype, device=like.device)
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+
+def gdn_decode(state, q, k, v, alpha, beta, out=None, *, num_k_heads: int, num_v_heads: int,
+               head_dim: int, stream=None):
+    """One token: advance ``state`` (fp32) in place and return the raw output o."""
+    torch = _torch()
+    B = state.shape[0]
+    NK, NV, D = _dims(None, num_k_heads, num_v_heads, head_dim)
+    if out is None:
+        out = _empty_rows(B, NV * D, torch.float32, state)
+    sp, pitch = _state(state, B, NV * D * D, torch.float32)
+    qp, qs, _ = _rows(q, B, NK * D, "q", torch.float32)
+    kp, ks, _ = _rows(k, B, NK * D, "k", torch.float32)
+    if qs != ks:
+        raise ValueError("q and k must share one row stride")
+    vp_, vs, _ = _rows(v, B, NV * D, "v", torch.float32)
+    ap, abs_, _ = _rows(alpha, B, NV, "alpha", torch.float32)
+    bp, bs, _ = _rows(beta, B, NV, "beta", torch.float32)
+    if abs_ != bs:
+        raise ValueError("alpha and beta must share one row stride")
+    op, os_, _ = _rows(out, B, NV * D, "out", torch.float32)
+    _check(_lib().gdn_decode(sp, pitch, qp, kp, qs, vp_, vs, ap, bp, abs_, op, os_, B, NK, NV, D,
+                             D, _stream(state, stream)), "gdn_decode")
+    return out
+
+
+def _norm_call(fn_name, state, state_dtype, q, k, v, alpha, beta, z, norm_weight, eps, out,
+               out_dtype, num_k_heads, num_v_heads, head_dim, stream, raw_ok):
+    torch = _torch()
+    B = state.shape[0]
+    NK, NV, D = _dims(norm_weight, num_k_heads, num_v_heads, head_dim)
+    if z is None and not raw_ok:
+        raise ValueError("z is required")
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else torch.float32
+    code = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16}.get(out_dtype)
+    if code is None:
+        raise TypeError(f"unsupported output dtype {out_dtype}")
+    if out is None:
+        out = _empty_rows(B, NV * D, out_dtype, state)
+    sp, pitch = _state(state, B, NV * D * D, state_dtype)
+    qp, qs, _ = _rows(q, B, NK * D, "q", torch.float32)
+    kp, ks, _ = _rows(k, B, NK * D, "k", torch.float32)
+    if qs != ks:
+        raise ValueError("q and k must share one row stride")
+    vp_, vs, _ = _rows(v, B, NV * D, "v", torch.float32)
+    ap, abs_, _ = _rows(alpha, B, NV, "alpha", torch.float32)
+    bp, bs, _ = _rows(beta, B, NV, "beta", torch.float32)
+    if abs_ != bs:
+        raise ValueError("alpha and beta must share one row stride")
+    if z is not None:
+        zp, zs, _ = _rows(z, B, NV * D, "z", torch.float32)
+        if norm_weight is None or norm_weight.dtype != torch.float32 or norm_weight.numel() < D:
+            raise ValueError("norm_weight must be fp32 [D]")
+        gp = norm_weight.data_ptr()
+    else:
+        zp, zs, gp = None, 0, None
+    op, os_, _ = _rows(out, B, NV * D, "out", out_dtype)
+    fn = getattr(_lib(), fn_name)
+    _check(fn(sp, pitch, qp, kp, qs, vp_, vs, ap, bp, abs_, zp, zs, gp, float(eps), op, code, os_,
+              B, NK, NV, D, D, _stream(state, stream)), fn_name)
+    return out
+
+
+def gdn_decode_norm(state, q, k, v, alpha, beta, z, norm_weight, eps: float = 1e-6, out=None, *,
+                    out_dtype=None, num_k_heads: int, num_v_heads: int,
+                    head_dim: Optional[int] = None, stream=None):
+    """One token with the fused gated RMS norm; returns y (fp32 or bf16)."""
+    return _norm_call("gdn_decode_norm", state, _torch().float32, q, k, v, alpha, beta, z,
+                      norm_weight, eps, out, out_dtype, num_k_heads, num_v_heads, head_dim,
+                      stream, raw_ok=False)
+
+
+def gdn_decode_f16state(state, q, k, v, alpha, beta, z=None, norm_weight=None, eps: float = 1e-6,
+                        out=None, *, out_dtype=None, num_k_heads: int, num_v_heads: int,
+                        head_dim: Optional[int] = None, stream=None):
+    """One token on a binary16 (``torch.float16``) state pool; y, or raw o if z is None."""
+    return _norm_call("gdn_decode_f16state", state, _torch().float16, q, k, v, alpha, beta, z,
+                      norm_weight, eps, out, out_dtype, num_k_heads, num_v_heads, head_dim,
+                      stream, raw_ok=True)
+
+
+def gdn_recurrence_seq(state, q, k, v, alpha, beta, z=None, norm_weight=None, eps: float = 1e-6,
+                       out=None, *, seq_len: int, num_k_heads: int, num_v_heads: int,
+                       head_dim: Optional[int] = None, stream=None):
+    """``seq_len`` tokens per sequence with the state on chip; returns o (or y) rows."""
+    torch = _torch()
+    B = state.shape[0]
+    T = int(seq_len)
+    NK, NV, D = _dims(norm_weight, num_k_heads, num_v_heads, head_dim)
+    rows = B * T
+    if out is None:
+        out = _empty_rows(rows, NV * D, torch.float32, state)
+    sp, pitch = _state(state, B, NV * D * D, torch.float32)
+    qp, qs, _ = _rows(q, rows, NK * D, "q", torch.float32)
+    kp, ks, _ = _rows(k, rows, NK * D, "k", torch.float32)
+    if qs != ks:
+        raise ValueError("q and k must share one row stride")
+    vp_, vs, _ = _rows(v, rows, NV * D, "v", torch.float32)
+    ap, abs_, _ = _rows(alpha, rows, NV, "alpha", torch.float32)
+    bp, bs, _ = _rows(beta, rows, NV, "beta", torch.float32)
+    if abs_ != bs:
+        raise ValueError("alpha and beta must share one row stride")
+    if z is not None:
+        zp, zs, _ = _rows(z, rows, NV * D, "z", torch.float32)
+        if norm_weight is None or norm_weight.dtype != torch.float32:
+            raise ValueError("norm_weight must be fp32 [D]")
+        gp = norm_weight.data_ptr()
+    else:
+        zp, zs, gp = None, 0, None
+    op, os_, _ = _rows(out, rows, NV * D, "out", torch.float32)
+    _check(_lib().gdn_recurrence_seq(sp, pitch, qp, kp, qs, vp_, vs, ap, bp, abs_, zp, zs, gp,
+                                     float(eps), op, os_, B, T, NK, NV, D, D,
+                                     _stream(state, stream)), "gdn_recurrence_seq")
+    return out
+
+
+def gdn_state_f32_to_f16(src, dst=None, stream=None):
+    """fp32 -> binary16 (RNE) over a whole pool; returns a ``torch.float16`` tensor."""
+    torch = _torch()
+    if src.dtype != torch.float32 or not src.is_contiguous():
+        raise ValueError("src must be a contiguous fp32 tensor")
+    if dst is None:
+        dst = torch.empty(src.shape, dtype=torch.float16, device=src.device)
+    if dst.dtype != torch.float16 or not dst.is_contiguous() or dst.numel() != src.numel():
+        raise ValueError("dst must be a contiguous float16 tensor of the same size")
+    _check(_lib().gdn_state_f32_to_f16(src.data_ptr(), dst.data_ptr(), src.numel(),
+                                       _stream(src, stream)), "gdn_state_f32_to_f16")
+    return dst
+
+
+def gdn_state_f16_to_f32(src, dst=None, stream=None):
+    """binary16 -> fp32 (exact) over a whole pool."""
+    torch = _torch()
+    if src.dtype != torch.float16 or not src.is_contiguous():
+        raise ValueError("src must be a contiguous float16 tensor")
+    if dst is None:
+        dst = torch.empty(src.shape, dtype=torch.float32, device=src.device)
+    if dst.dtype != torch.float32 or not dst.is_contiguous() or dst.numel() != src.numel():
+        raise ValueError("dst must be a contiguous fp32 tensor of the same size")
+    _check(_lib().gdn_state_f16_to_f32(src.data_ptr(), dst.data_ptr(), src.numel(),
+                                       _stream(src, stream)), "gdn_state_f16_to_f32")
+    return dst

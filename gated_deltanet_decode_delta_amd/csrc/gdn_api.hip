@@ -1,0 +1,271 @@
+// gdn_api.hip -- the extern "C" entry points of libgdn.so (contract: gdn.h).
+//
+// Every call validates its arguments on the host first -- shapes, strides,
+// alignment and address-range overlap -- and returns before any HIP call if
+// one is wrong, so a rejected call leaves every buffer untouched.  Only then is
+// the kernel launched on the caller's stream.  No allocation, no
+// synchronisation, no printing.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/gdn.h"
+#include "gdn_launch.h"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+struct Span {
+    __int128 lo = 0, hi = 0;  // byte range [lo, hi); empty when lo == hi
+};
+
+constexpr __int128 kMaxBytes = (__int128)1 << 62;
+
+// Bytes touched by `rows` rows of `width` elements, `stride` elements apart.
+bool make_span(const void *p, int64_t rows, int64_t stride, int64_t width, int64_t elem, Span *out) {
+    if (rows <= 0 || width <= 0) { *out = Span{}; return true; }
+    const __int128 n = (__int128)(rows - 1) * stride + width;
+    const __int128 bytes = n * elem;
+    if (bytes > kMaxBytes) return false;
+    out->lo = (__int128)(uintptr_t)p;
+    out->hi = out->lo + bytes;
+    return true;
+}
+
+bool overlap(const Span &a, const Span &b) {
+    if (a.lo == a.hi || b.lo == b.hi) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned(const void *p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
+
+bool supported_dim(int32_t d) {
+    return d == 4 || d == 8 || d == 16 || d == 32 || d == 64 || d == 128 || d == 256;
+}
+
+struct Call {
+    const void *state;
+    int64_t pitch;
+    int state_elem;     // 4 or 2 bytes
+    const float *q, *k;
+    int64_t qk_stride;
+    const float *v;
+    int64_t v_stride;
+    const float *alpha, *beta;
+    int64_t ab_stride;
+    const float *z;     // may be NULL when the raw output is asked for
+    int64_t z_stride;
+    const float *gn;
+    float eps;
+    bool norm;
+    const void *out;
+    int out_elem;
+    int64_t out_stride;
+    int32_t batch, seq_len, nk, nv, dk, dv;
+};
+
+gdn_status validate(const Call &c, bool *empty) {
+    *empty = false;
+    if (c.batch < 0 || c.seq_len < 0) return GDN_ERR_SHAPE;
+    if (c.nk <= 0 || c.nv <= 0 || c.nv % c.nk != 0) return GDN_ERR_SHAPE;
+    if (c.dk <= 0 || c.dv <= 0) return GDN_ERR_SHAPE;
+    if (c.dk != c.dv || !supported_dim(c.dk)) return GDN_ERR_UNSUPPORTED;
+    if ((int64_t)c.batch * c.nv > INT32_MAX) return GDN_ERR_SHAPE;
+    if (c.norm && (!isfinite(c.eps) || c.eps < 0.0f)) return GDN_ERR_ARG;
+    if (c.batch == 0 || c.seq_len == 0) { *empty = true; return GDN_OK; }
+
+    if (!c.state || !c.q || !c.k || !c.v || !c.alpha || !c.beta || !c.out) return GDN_ERR_NULL;
+    if (c.norm && (!c.z || !c.gn)) return GDN_ERR_NULL;
+
+    const int64_t D = c.dk;
+    const int64_t rows = (int64_t)c.batch * c.seq_len;
+    const int64_t slot = (int64_t)c.nv * D * D;
+    const int64_t vw = (int64_t)c.nv * D;
+    const int64_t qkw = (int64_t)c.nk * D;
+    // strides: large enough for their row (only meaningful with more than one row)
+    if (c.batch > 1 && c.pitch < slot) return GDN_ERR_STRIDE;
+    if (rows > 1 && (c.qk_stride < qkw || c.v_stride < vw || c.ab_stride < c.nv ||
+                     c.out_stride < vw || (c.norm && c.z_stride < vw)))
+        return GDN_ERR_STRIDE;
+    // alignment of the vector-accessed arrays
+    const int64_t state_vec = 16 / c.state_elem;
+    if (!aligned(c.state, 16) || (c.batch > 1 && c.pitch % state_vec != 0)) return GDN_ERR_STRIDE;
+    if (!aligned(c.q, 16) || !aligned(c.k, 16) || !aligned(c.v, 16) || !aligned(c.out, 16))
+        return GDN_ERR_STRIDE;
+    if (rows > 1 && (c.qk_stride % 4 || c.v_stride % 4 || c.out_stride % 4)) return GDN_ERR_STRIDE;
+    if (c.norm && (!aligned(c.z, 16) || (rows > 1 && c.z_stride % 4))) return GDN_ERR_STRIDE;
+    if (!aligned(c.alpha, 4) || !aligned(c.beta, 4) || (c.norm && !aligned(c.gn, 4)))
+        return GDN_ERR_STRIDE;
+
+    // address ranges
+    Span st, q, k, v, al, be, z, gn, out;
+    bool ok = make_span(c.state, c.batch, c.pitch, slot, c.state_elem, &st) &&
+              make_span(c.q, rows, c.qk_stride, qkw, 4, &q) &&
+              make_span(c.k, rows, c.qk_stride, qkw, 4, &k) &&
+              make_span(c.v, rows, c.v_stride, vw, 4, &v) &&
+              make_span(c.alpha, rows, c.ab_stride, c.nv, 4, &al) &&
+              make_span(c.beta, rows, c.ab_stride, c.nv, 4, &be) &&
+              make_span(c.out, rows, c.out_stride, vw, c.out_elem, &out);
+    if (c.norm) ok = ok && make_span(c.z, rows, c.z_stride, vw, 4, &z) && make_span(c.gn, 1, D, D, 4, &gn);
+    if (!ok) return GDN_ERR_STRIDE;
+    const Span *inputs[] = {&q, &k, &v, &al, &be, &z, &gn};
+    for (const Span *in : inputs)
+        if (overlap(st, *in) || overlap(out, *in)) return GDN_ERR_ALIAS;
+    if (overlap(st, out)) return GDN_ERR_ALIAS;
+    return GDN_OK;
+}
+
+gdn::StepArgs to_args(const Call &c, void *state, void *out) {
+    gdn::StepArgs a;
+    a.state = state;
+    a.pitch = c.pitch;
+    a.q = c.q;
+    a.k = c.k;
+    a.qk_stride = c.qk_stride;
+    a.v = c.v;
+    a.v_stride = c.v_stride;
+    a.alpha = c.alpha;
+    a.beta = c.beta;
+    a.ab_stride = c.ab_stride;
+    a.z = c.z;
+    a.z_stride = c.z_stride;
+    a.gn = c.gn;
+    a.eps = c.eps;
+    a.scale = (float)(1.0 / sqrt((double)c.dk));
+    a.out = out;
+    a.out_stride = c.out_stride;
+    a.batch = c.batch;
+    a.seq_len = c.seq_len;
+    a.nk = c.nk;
+    a.nv = c.nv;
+    return a;
+}
+
+gdn_status finish(hipError_t e) {
+    if (e == hipSuccess) return GDN_OK;
+    g_last_hip_error = (int32_t)e;
+    return GDN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_decode(float *state, int64_t state_seq_stride, const float *q, const float *k,
+                      int64_t qk_stride, const float *v, int64_t v_stride, const float *alpha,
+                      const float *beta, int64_t ab_stride, float *out, int64_t out_stride,
+                      int32_t batch, int32_t num_k_heads, int32_t num_v_heads, int32_t k_dim,
+                      int32_t v_dim, void *stream) {
+    Call c{state, state_seq_stride, 4, q, k, qk_stride, v, v_stride, alpha, beta, ab_stride,
+           nullptr, 0, nullptr, 0.0f, false, out, 4, out_stride,
+           batch, 1, num_k_heads, num_v_heads, k_dim, v_dim};
+    bool empty;
+    gdn_status s = validate(c, &empty);
+    if (s != GDN_OK || empty) return s;
+    return finish(gdn::launch_decode(to_args(c, state, out), k_dim, false, gdn::kOutRawF32,
+                                     (hipStream_t)stream));
+}
+
+gdn_status gdn_decode_norm(float *state, int64_t state_seq_stride, const float *q, const float *k,
+                           int64_t qk_stride, const float *v, int64_t v_stride, const float *alpha,
+                           const float *beta, int64_t ab_stride, const float *z, int64_t z_stride,
+                           const float *norm_weight, float eps, void *out, int32_t out_dtype,
+                           int64_t out_stride, int32_t batch, int32_t num_k_heads,
+                           int32_t num_v_heads, int32_t k_dim, int32_t v_dim, void *stream) {
+    if (out_dtype != GDN_F32 && out_dtype != GDN_BF16) return GDN_ERR_DTYPE;
+    Call c{state, state_seq_stride, 4, q, k, qk_stride, v, v_stride, alpha, beta, ab_stride,
+           z, z_stride, norm_weight, eps, true, out, out_dtype == GDN_F32 ? 4 : 2, out_stride,
+           batch, 1, num_k_heads, num_v_heads, k_dim, v_dim};
+    bool empty;
+    gdn_status s = validate(c, &empty);
+    if (s != GDN_OK || empty) return s;
+    return finish(gdn::launch_decode(to_args(c, state, out), k_dim, false,
+                                     out_dtype == GDN_F32 ? gdn::kOutNormF32 : gdn::kOutNormBF16,
+                                     (hipStream_t)stream));
+}
+
+gdn_status gdn_decode_f16state(uint16_t *state, int64_t state_seq_stride, const float *q,
+                               const float *k, int64_t qk_stride, const float *v, int64_t v_stride,
+                               const float *alpha, const float *beta, int64_t ab_stride,
+                               const float *z, int64_t z_stride, const float *norm_weight,
+                               float eps, void *out, int32_t out_dtype, int64_t out_stride,
+                               int32_t batch, int32_t num_k_heads, int32_t num_v_heads,
+                               int32_t k_dim, int32_t v_dim, void *stream) {
+    const bool norm = z != nullptr;
+    if (out_dtype != GDN_F32 && out_dtype != GDN_BF16) return GDN_ERR_DTYPE;
+    if (!norm && out_dtype != GDN_F32) return GDN_ERR_DTYPE;
+    Call c{state, state_seq_stride, 2, q, k, qk_stride, v, v_stride, alpha, beta, ab_stride,
+           z, z_stride, norm_weight, eps, norm, out, out_dtype == GDN_F32 ? 4 : 2, out_stride,
+           batch, 1, num_k_heads, num_v_heads, k_dim, v_dim};
+    bool empty;
+    gdn_status s = validate(c, &empty);
+    if (s != GDN_OK || empty) return s;
+    const gdn::OutMode mode = !norm ? gdn::kOutRawF32
+                                    : (out_dtype == GDN_F32 ? gdn::kOutNormF32 : gdn::kOutNormBF16);
+    return finish(gdn::launch_decode(to_args(c, state, out), k_dim, true, mode, (hipStream_t)stream));
+}
+
+gdn_status gdn_recurrence_seq(float *state, int64_t state_seq_stride, const float *q,
+                              const float *k, int64_t qk_stride, const float *v, int64_t v_stride,
+                              const float *alpha, const float *beta, int64_t ab_stride,
+                              const float *z, int64_t z_stride, const float *norm_weight,
+                              float eps, float *out, int64_t out_stride, int32_t batch,
+                              int32_t seq_len, int32_t num_k_heads, int32_t num_v_heads,
+                              int32_t k_dim, int32_t v_dim, void *stream) {
+    const bool norm = z != nullptr;
+    Call c{state, state_seq_stride, 4, q, k, qk_stride, v, v_stride, alpha, beta, ab_stride,
+           z, z_stride, norm_weight, eps, norm, out, 4, out_stride,
+           batch, seq_len, num_k_heads, num_v_heads, k_dim, v_dim};
+    bool empty;
+    gdn_status s = validate(c, &empty);
+    if (s != GDN_OK || empty) return s;
+    return finish(gdn::launch_seq(to_args(c, state, out), k_dim,
+                                  norm ? gdn::kOutNormF32 : gdn::kOutRawF32, (hipStream_t)stream));
+}
+
+static gdn_status check_convert(const void *src, const void *dst, int64_t n, int src_elem,
+                                 int dst_elem, bool *empty) {
+    *empty = false;
+    if (n < 0) return GDN_ERR_SHAPE;
+    if (n == 0) { *empty = true; return GDN_OK; }
+    if (!src || !dst) return GDN_ERR_NULL;
+    if (!aligned(src, 16) || !aligned(dst, 16)) return GDN_ERR_STRIDE;
+    Span a, b;
+    if (!make_span(src, 1, n, n, src_elem, &a) || !make_span(dst, 1, n, n, dst_elem, &b))
+        return GDN_ERR_STRIDE;
+    if (overlap(a, b)) return GDN_ERR_ALIAS;
+    return GDN_OK;
+}
+
+gdn_status gdn_state_f32_to_f16(const float *src, uint16_t *dst, int64_t n, void *stream) {
+    bool empty;
+    gdn_status s = check_convert(src, dst, n, 4, 2, &empty);
+    if (s != GDN_OK || empty) return s;
+    return finish(gdn::launch_f32_to_f16(src, dst, n, (hipStream_t)stream));
+}
+
+gdn_status gdn_state_f16_to_f32(const uint16_t *src, float *dst, int64_t n, void *stream) {
+    bool empty;
+    gdn_status s = check_convert(src, dst, n, 2, 4, &empty);
+    if (s != GDN_OK || empty) return s;
+    return finish(gdn::launch_f16_to_f32(src, dst, n, (hipStream_t)stream));
+}
+
+const char *gdn_status_string(gdn_status s) {
+    switch (s) {
+        case GDN_OK: return "GDN_OK";
+        case GDN_ERR_NULL: return "GDN_ERR_NULL: a required pointer is NULL";
+        case GDN_ERR_SHAPE: return "GDN_ERR_SHAPE: invalid batch, length or head counts";
+        case GDN_ERR_STRIDE: return "GDN_ERR_STRIDE: stride/pitch too small or misaligned";
+        case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED: head dims must be equal powers of two in [4, 256]";
+        case GDN_ERR_ALIAS: return "GDN_ERR_ALIAS: state/output overlaps another buffer";
+        case GDN_ERR_DTYPE: return "GDN_ERR_DTYPE: unsupported output dtype";
+        case GDN_ERR_HIP: return "GDN_ERR_HIP: kernel launch failed";
+        case GDN_ERR_ARG: return "GDN_ERR_ARG: invalid scalar argument";
+    }
+    return "unknown gdn_status";
+}
+
+int32_t gdn_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

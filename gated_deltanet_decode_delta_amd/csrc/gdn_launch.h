@@ -1,0 +1,43 @@
+// gdn_launch.h -- internal interface between the C ABI (gdn_api.hip) and the
+// kernel translation units.  Not installed; the public contract is gdn.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// Everything a decode or sequence launch needs; strides in elements.
+struct StepArgs {
+    void *state;             // fp32 or binary16 pool
+    int64_t pitch;           // elements of the state type per sequence slot
+    const float *q;
+    const float *k;
+    int64_t qk_stride;
+    const float *v;
+    int64_t v_stride;
+    const float *alpha;
+    const float *beta;
+    int64_t ab_stride;
+    const float *z;          // NULL: raw output
+    int64_t z_stride;
+    const float *gn;
+    float eps;
+    float scale;             // 1 / sqrt(Dk)
+    void *out;
+    int64_t out_stride;
+    int32_t batch;
+    int32_t seq_len;         // 1 for decode
+    int32_t nk;
+    int32_t nv;
+};
+
+enum OutMode { kOutRawF32 = 0, kOutNormF32 = 1, kOutNormBF16 = 2 };
+
+hipError_t launch_decode(const StepArgs &a, int dim, bool f16_state, OutMode mode,
+                         hipStream_t stream);
+hipError_t launch_seq(const StepArgs &a, int dim, OutMode mode, hipStream_t stream);
+hipError_t launch_f32_to_f16(const float *src, uint16_t *dst, int64_t n, hipStream_t stream);
+hipError_t launch_f16_to_f32(const uint16_t *src, float *dst, int64_t n, hipStream_t stream);
+
+}  // namespace gdn

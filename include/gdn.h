@@ -1,0 +1,182 @@
+/*
+ * gdn.h -- C ABI of libgdn.so: the gated delta rule (Gated DeltaNet) state
+ * recurrence on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (logicaffeine "codegen_cuda/gdn.rs", kernel `gdn_step`): for
+ * sequence b and value head h, with key head g = h mod NK (tiled pairing, the
+ * `ggml_repeat` broadcast, NOT h / (NV/NK)), the head's Dv x Dk state S is
+ * advanced by one token as
+ *
+ *     u = S k_g,  w = S q_g,  coef_i = beta (v_i - alpha u_i)
+ *     o_i = (alpha w_i + coef_i (k_g . q_g)) / sqrt(Dk)          (= (S' q_g)_i / sqrt(Dk))
+ *     S  <- alpha S + coef k_g^T                                 (= alpha S (I - beta k k^T) + beta v k^T)
+ *
+ * and optionally followed by the gated RMS norm of the same page's kernel
+ * `gdn_gate_norm`: y_i = gn_i o_i / sqrt(mean_j o_j^2 + eps) * z_i sigmoid(z_i)
+ * (norm, then weight, then gate).  alpha is a linear decay multiplier and beta
+ * the write strength, one scalar each per (token, value head).
+ *
+ * The entry points mirror the launchers of metrale "layers/ops/ssm_gdn_a.rs"
+ * (`gdn_decode`, `gdn_decode_f32_strided_norm`, `gdn_decode_f16_strided_norm`,
+ * `gdn_prefill_regresident`, `ssm_h_state_f32_to_f16`, `ssm_h_state_f16_to_f32`):
+ * device pointers, element strides per sequence row, a state slot pitch, a
+ * stream, and an error code instead of a panic.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers   Every array pointer is a DEVICE pointer (hipMalloc / torch CUDA
+ *            tensors).  The caller owns all memory; the library allocates no
+ *            device memory, keeps no state except a thread-local last HIP error,
+ *            and never synchronises.  Calls are asynchronous on `stream`
+ *            (a hipStream_t; NULL = the null stream).
+ * Strides    All strides and pitches count ELEMENTS of the array's own type,
+ *            never bytes.  Sequence b's q/k row starts at q + b*qk_stride
+ *            (key head g at + g*Dk); v, z and out rows at + b*stride (value
+ *            head h at + h*Dv); alpha/beta at + b*ab_stride + h.  The state slot
+ *            of sequence b starts at state + b*state_seq_stride; value head h's
+ *            tile at + h*Dv*Dk, row-major with row i = value index and column
+ *            j = key index (key index contiguous).  A pitch larger than
+ *            NV*Dv*Dk leaves a pad that is never read or written.
+ * Alignment  state, q, k, v, z and out base pointers must be 16-byte aligned,
+ *            and their row strides / pitch a multiple of 4 elements (of 8 for a
+ *            binary16 state pitch).  alpha, beta and norm_weight need only
+ *            natural (4-byte) alignment.  Anything else returns GDN_ERR_STRIDE:
+ *            there is no slow fallback path.
+ * Shapes     k_dim == v_dim, a power of two in [4, 256]; num_v_heads a
+ *            multiple of num_k_heads; batch (and seq_len) >= 0.  A zero batch
+ *            or seq_len is a valid no-op (nothing is read, written or launched).
+ * Aliasing   Read-only inputs may alias each other (e.g. q|k|v inside one packed
+ *            projection row).  The state and the output must not overlap any
+ *            input or each other: GDN_ERR_ALIAS (checked on address ranges).
+ * Errors     Validation happens before any HIP call; on failure no buffer is
+ *            touched and nothing is launched.  A failed launch returns
+ *            GDN_ERR_HIP and gdn_last_hip_error() gives the hipError_t.
+ *            Nothing prints, aborts or throws across the ABI.
+ * Results    Bitwise deterministic run to run: fixed reduction orders, no
+ *            atomics.  Non-finite inputs propagate; finite inputs in the ranges
+ *            the recurrence is used with never produce NaN or Inf.
+ * Threads    The functions are re-entrant; concurrent calls on distinct
+ *            streams are safe when their output/state ranges are disjoint.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gdn_status {
+    GDN_OK = 0,
+    GDN_ERR_NULL = 1,        /* a required pointer is NULL                                   */
+    GDN_ERR_SHAPE = 2,       /* negative batch/seq_len, non-positive heads, NV % NK != 0      */
+    GDN_ERR_STRIDE = 3,      /* stride/pitch too small for its row, or misaligned pointer     */
+    GDN_ERR_UNSUPPORTED = 4, /* k_dim != v_dim, or not a power of two in [4, 256]             */
+    GDN_ERR_ALIAS = 5,       /* state/out overlaps an input or each other; converter in-place */
+    GDN_ERR_DTYPE = 6,       /* out_dtype is not GDN_F32 / GDN_BF16 (or not allowed here)     */
+    GDN_ERR_HIP = 7,         /* the kernel launch failed; see gdn_last_hip_error()            */
+    GDN_ERR_ARG = 8          /* a scalar argument is invalid (eps negative or not finite)     */
+} gdn_status;
+
+enum { GDN_F32 = 0, GDN_BF16 = 1 };
+
+/*
+ * gdn_decode -- one token for every (sequence, value head) pair: the state is
+ * advanced in place and the raw output o is written as fp32.
+ * Source: logicaffeine codegen_cuda/gdn.rs, kernel `gdn_step`; metrale
+ * ssm_gdn_a.rs, launchers `gdn_decode` and `gdn_decode_f32_strided`.
+ *   state  fp32 [batch][state_seq_stride], slot layout as above (read+write)
+ *   q, k   fp32 rows of >= num_k_heads*k_dim, qk_stride apart (read)
+ *   v      fp32 rows of >= num_v_heads*v_dim, v_stride apart (read)
+ *   alpha, beta  fp32 rows of >= num_v_heads, ab_stride apart (read)
+ *   out    fp32 rows of num_v_heads*v_dim, out_stride apart (write)
+ */
+gdn_status gdn_decode(float *state, int64_t state_seq_stride,
+                      const float *q, const float *k, int64_t qk_stride,
+                      const float *v, int64_t v_stride,
+                      const float *alpha, const float *beta, int64_t ab_stride,
+                      float *out, int64_t out_stride,
+                      int32_t batch, int32_t num_k_heads, int32_t num_v_heads,
+                      int32_t k_dim, int32_t v_dim, void *stream);
+
+/*
+ * gdn_decode_norm -- gdn_decode with the gated RMS norm fused into the same
+ * kernel: out receives y (fp32 or bf16 rounded to nearest-even) and no raw o is
+ * written anywhere.  Source: logicaffeine codegen_cuda/gdn.rs, kernel
+ * `gdn_gate_norm`; metrale ssm_gdn_a.rs, launchers `gdn_decode_f32_norm` and
+ * `gdn_decode_f32_strided_norm`.
+ *   z            fp32 rows of >= num_v_heads*v_dim, z_stride apart (read)
+ *   norm_weight  fp32 [v_dim], shared by all heads (read)
+ *   eps          >= 0, inside the square root (the model uses 1e-6)
+ *   out          out_dtype (GDN_F32 or GDN_BF16) rows, out_stride apart (write)
+ */
+gdn_status gdn_decode_norm(float *state, int64_t state_seq_stride,
+                           const float *q, const float *k, int64_t qk_stride,
+                           const float *v, int64_t v_stride,
+                           const float *alpha, const float *beta, int64_t ab_stride,
+                           const float *z, int64_t z_stride, const float *norm_weight, float eps,
+                           void *out, int32_t out_dtype, int64_t out_stride,
+                           int32_t batch, int32_t num_k_heads, int32_t num_v_heads,
+                           int32_t k_dim, int32_t v_dim, void *stream);
+
+/*
+ * gdn_decode_f16state -- the IEEE binary16 state twin of gdn_decode_norm.
+ * The state is read as binary16, all arithmetic is fp32, and the updated state
+ * is rounded to nearest-even binary16 on store (subnormals kept).
+ * state_seq_stride is the slot pitch in HALVES (it depends on how the pool was
+ * sized, not on the head dims).  z == NULL selects the raw output o, which then
+ * must be GDN_F32; otherwise norm_weight is required and out is y as in
+ * gdn_decode_norm.  Source: metrale ssm_gdn_a.rs, launcher
+ * `gdn_decode_f16_strided_norm`.
+ */
+gdn_status gdn_decode_f16state(uint16_t *state, int64_t state_seq_stride,
+                               const float *q, const float *k, int64_t qk_stride,
+                               const float *v, int64_t v_stride,
+                               const float *alpha, const float *beta, int64_t ab_stride,
+                               const float *z, int64_t z_stride, const float *norm_weight,
+                               float eps, void *out, int32_t out_dtype, int64_t out_stride,
+                               int32_t batch, int32_t num_k_heads, int32_t num_v_heads,
+                               int32_t k_dim, int32_t v_dim, void *stream);
+
+/*
+ * gdn_recurrence_seq -- seq_len tokens of every (sequence, value head), the
+ * state held on chip across tokens: each slot is read once at the start and
+ * written once at the end.  Token t of sequence b uses input row
+ * r = b*seq_len + t of q, k, v, z, alpha, beta and writes output row r.
+ * z == NULL gives the raw o; otherwise the fused gated norm y (norm_weight
+ * required).  Output is fp32.  Source: metrale ssm_gdn_a.rs, launcher
+ * `gdn_prefill_regresident` (token-sequential recurrence with the state in
+ * registers), generalised to any supported head dim.
+ */
+gdn_status gdn_recurrence_seq(float *state, int64_t state_seq_stride,
+                              const float *q, const float *k, int64_t qk_stride,
+                              const float *v, int64_t v_stride,
+                              const float *alpha, const float *beta, int64_t ab_stride,
+                              const float *z, int64_t z_stride, const float *norm_weight,
+                              float eps, float *out, int64_t out_stride,
+                              int32_t batch, int32_t seq_len, int32_t num_k_heads,
+                              int32_t num_v_heads, int32_t k_dim, int32_t v_dim, void *stream);
+
+/*
+ * State pool converters: n elements, fp32 -> binary16 with round to
+ * nearest-even (subnormals kept, overflow to infinity, NaN stays NaN), and
+ * binary16 -> fp32 (exact).  src and dst must not overlap (an in-place
+ * narrowing would race): GDN_ERR_ALIAS.  Both 16-byte aligned.  n == 0 is a
+ * no-op.  Source: metrale ssm_gdn_a.rs, `ssm_h_state_f32_to_f16` and
+ * `ssm_h_state_f16_to_f32`.
+ */
+gdn_status gdn_state_f32_to_f16(const float *src, uint16_t *dst, int64_t n, void *stream);
+gdn_status gdn_state_f16_to_f32(const uint16_t *src, float *dst, int64_t n, void *stream);
+
+/* Static, human-readable name of a status code. */
+const char *gdn_status_string(gdn_status s);
+
+/* The hipError_t of the calling thread's last GDN_ERR_HIP (0 if none yet). */
+int32_t gdn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

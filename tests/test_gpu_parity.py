@@ -1,0 +1,522 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Every case draws seeded inputs, runs the library on cuda:0 and the oracle on
+the host on the same arrays, and compares per head (tile or output vector):
+max |gpu - oracle| / max |oracle| must stay under the stated tolerance --
+1e-5 for one fp32 step, 1e-4 after chained steps (up to 4096), 3e-3 for a
+binary16 state; bf16 outputs may also differ by half a bf16 ulp.  Full-size
+workloads are checked on every head when the oracle is fast enough, otherwise
+on sampled heads that the oracle computes one by one.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle as orc
+from gated_deltanet_decode_delta_amd import inputs
+from gpu_util import bf16_ok, dev, host, out_err, tile_err
+
+pytestmark = pytest.mark.gpu
+
+TOL_STEP = 1e-5
+TOL_CHAIN = 1e-4
+TOL_F16 = 3e-3
+
+
+@pytest.fixture(scope="module")
+def g():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gated_deltanet_decode_delta_amd as gdn
+    gdn.lib()
+    return gdn
+
+
+def say(*a):
+    print("[case]", *a, file=sys.stderr, flush=True)
+
+
+def _dev_case(c):
+    return dict(q=dev(c.q), k=dev(c.k), v=dev(c.v), z=dev(c.z), alpha=dev(c.alpha),
+                beta=dev(c.beta), gn=dev(c.gn))
+
+
+def _sample_heads(B, NV, n, seed):
+    r = np.random.Generator(np.random.PCG64(seed))
+    idx = r.choice(B * NV, size=min(n, B * NV), replace=False)
+    return sorted((int(i) // NV, int(i) % NV) for i in idx)
+
+
+# --------------------------------------------------------------------------- 1
+def test_tiny_config_all_paths(g):
+    """Miniature (NV=2, NK=1, D=4, 8 tokens): decode, decode_norm and the
+    sequence kernel (raw and normed) against the oracle token by token."""
+    c = inputs.config_case("tiny")
+    B, T, NK, NV, D = c.B, c.T, c.NK, c.NV, c.D
+    say("tiny", B, T, NK, NV, D)
+    ref_state = c.state.copy()
+    ref_y = orc.seq(ref_state, c.q, c.k, c.v, c.alpha, c.beta, B=B, T=T, NK=NK, NV=NV, Dk=D, Dv=D,
+                    z=c.z, gn=c.gn)
+    ref_state_raw = c.state.copy()
+    ref_o = orc.seq(ref_state_raw, c.q, c.k, c.v, c.alpha, c.beta, B=B, T=T, NK=NK, NV=NV, Dk=D,
+                    Dv=D)
+    d = _dev_case(c)
+    st_n, st_r = dev(c.state), dev(c.state)
+    for t in range(T):
+        sl = slice(t, t + 1)
+        y = g.gdn_decode_norm(st_n, d["q"][sl], d["k"][sl], d["v"][sl], d["alpha"][sl],
+                              d["beta"][sl], d["z"][sl], d["gn"], c.eps, num_k_heads=NK,
+                              num_v_heads=NV)
+        o = g.gdn_decode(st_r, d["q"][sl], d["k"][sl], d["v"][sl], d["alpha"][sl], d["beta"][sl],
+                         num_k_heads=NK, num_v_heads=NV, head_dim=D)
+        st_ref_t = c.state.copy()
+        orc.seq(st_ref_t, c.q[:t + 1], c.k[:t + 1], c.v[:t + 1], c.alpha[:t + 1], c.beta[:t + 1],
+                B=1, T=t + 1, NK=NK, NV=NV, Dk=D, Dv=D)
+        assert out_err(host(y), ref_y[sl], NV, D) < TOL_STEP, t
+        assert out_err(host(o), ref_o[sl], NV, D) < TOL_STEP, t
+        assert tile_err(host(st_r), st_ref_t, NV, D) < TOL_STEP, t
+        assert tile_err(host(st_n), st_ref_t, NV, D) < TOL_STEP, t
+    st_s = dev(c.state)
+    o_seq = g.gdn_recurrence_seq(st_s, d["q"], d["k"], d["v"], d["alpha"], d["beta"], seq_len=T,
+                                 num_k_heads=NK, num_v_heads=NV, head_dim=D)
+    assert out_err(host(o_seq), ref_o, NV, D) < TOL_STEP
+    assert tile_err(host(st_s), ref_state_raw, NV, D) < TOL_STEP
+    st_s = dev(c.state)
+    y_seq = g.gdn_recurrence_seq(st_s, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["z"],
+                                 d["gn"], c.eps, seq_len=T, num_k_heads=NK, num_v_heads=NV)
+    assert out_err(host(y_seq), ref_y, NV, D) < TOL_STEP
+    assert tile_err(host(st_s), ref_state, NV, D) < TOL_STEP
+
+
+# --------------------------------------------------------------------------- 2
+def test_real_head_layers(g):
+    """Real head shape (B=1, NV=48, NK=16, D=128), fused norm fp32, several of
+    the 48 independent layer states, every head checked."""
+    for layer in range(4):
+        c = inputs.make_case(200 + layer, B=1, NK=16, NV=48, D=128)
+        say("real_head layer", layer)
+        ref_state = c.state.copy()
+        ref = orc.decode(ref_state, c.q, c.k, c.v, c.alpha, c.beta, B=1, NK=16, NV=48, Dk=128,
+                         Dv=128, z=c.z, gn=c.gn, eps=c.eps)
+        d = _dev_case(c)
+        st = dev(c.state)
+        y = g.gdn_decode_norm(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["z"], d["gn"],
+                              c.eps, num_k_heads=16, num_v_heads=48)
+        assert out_err(host(y), ref, 48, 128) < TOL_STEP
+        assert tile_err(host(st), ref_state, 48, 128) < TOL_STEP
+
+
+# --------------------------------------------------------------------------- 3
+def test_batched_padded_pool_100_calls(g):
+    """B=64 with a 1.25x slot pitch (NaN pads), fused norm fp32: every head after
+    call 1, sampled heads after call 100; pads untouched."""
+    import torch
+    c = inputs.config_case("batched")
+    B, NK, NV, D = c.B, c.NK, c.NV, c.D
+    say("batched B=64 pitch", c.pitch)
+    d = _dev_case(c)
+    st = dev(c.state)
+    ref_state = c.state.copy()
+    ref = orc.decode(ref_state, c.q, c.k, c.v, c.alpha, c.beta, B=B, NK=NK, NV=NV, Dk=D, Dv=D,
+                     z=c.z, gn=c.gn, eps=c.eps)
+    y = g.gdn_decode_norm(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["z"], d["gn"],
+                          c.eps, num_k_heads=NK, num_v_heads=NV)
+    got_state = host(st)
+    assert out_err(host(y), ref, NV, D) < TOL_STEP
+    assert tile_err(got_state, ref_state, NV, D) < TOL_STEP
+    assert np.isnan(got_state[:, NV * D * D:]).all()
+    heads = _sample_heads(B, NV, 12, 33)
+    for _ in range(99):
+        y = g.gdn_decode_norm(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["z"], d["gn"],
+                              c.eps, out=y, num_k_heads=NK, num_v_heads=NV)
+    for _ in range(99):
+        ref = orc.decode(ref_state, c.q, c.k, c.v, c.alpha, c.beta, B=B, NK=NK, NV=NV, Dk=D,
+                         Dv=D, z=c.z, gn=c.gn, eps=c.eps, heads=heads)
+    got_state, got_y = host(st), host(y)
+    assert np.isnan(got_state[:, NV * D * D:]).all()
+    for (b, h) in heads:
+        sl = slice(h * D * D, (h + 1) * D * D)
+        assert tile_err(got_state[b:b + 1, sl], ref_state[b:b + 1, sl], 1, D) < TOL_CHAIN, (b, h)
+        osl = slice(h * D, (h + 1) * D)
+        assert out_err(got_y[b:b + 1, osl], ref[b:b + 1, osl], 1, D) < TOL_CHAIN, (b, h)
+    del torch
+
+
+def test_batched_raw_decode_and_packed_rows(g):
+    """gdn_decode (raw o) at B=64, and q|k|v read from one packed projection row
+    ([B, 2*NK*D + NV*D]) with z from a wider row, through element strides."""
+    c = inputs.config_case("batched")
+    B, NK, NV, D = c.B, c.NK, c.NV, c.D
+    say("batched raw + packed rows")
+    ref_state = c.state.copy()
+    ref_o = orc.decode(ref_state, c.q, c.k, c.v, c.alpha, c.beta, B=B, NK=NK, NV=NV, Dk=D, Dv=D)
+    d = _dev_case(c)
+    st = dev(c.state)
+    o = g.gdn_decode(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"], num_k_heads=NK,
+                     num_v_heads=NV, head_dim=D)
+    assert out_err(host(o), ref_o, NV, D) < TOL_STEP
+    assert tile_err(host(st), ref_state, NV, D) < TOL_STEP
+
+    qk = NK * D
+    W = 2 * qk + NV * D
+    packed = np.zeros((B, W), np.float32)
+    packed[:, :qk], packed[:, qk:2 * qk], packed[:, 2 * qk:] = c.q, c.k, c.v
+    zrow = np.zeros((B, 2 * qk + 2 * NV * D), np.float32)
+    zrow[:, 2 * qk + NV * D:] = c.z
+    ab = np.zeros((B, 2 * NV), np.float32)
+    ab[:, :NV], ab[:, NV:] = c.beta, c.alpha
+    pk, zr, abd = dev(packed), dev(zrow), dev(ab)
+    ref_state = c.state.copy()
+    ref_y = orc.decode(ref_state, c.q, c.k, c.v, c.alpha, c.beta, B=B, NK=NK, NV=NV, Dk=D, Dv=D,
+                       z=c.z, gn=c.gn, eps=c.eps)
+    st = dev(c.state)
+    y = g.gdn_decode_norm(st, pk[:, :qk], pk[:, qk:2 * qk], pk[:, 2 * qk:], abd[:, NV:],
+                          abd[:, :NV], zr[:, 2 * qk + NV * D:], d["gn"], c.eps, num_k_heads=NK,
+                          num_v_heads=NV)
+    assert out_err(host(y), ref_y, NV, D) < TOL_STEP
+    assert tile_err(host(st), ref_state, NV, D) < TOL_STEP
+
+
+# --------------------------------------------------------------------------- 4
+def test_fp16_state_full_batch(g):
+    """B=256 binary16 pool from an fp32 N(0, 0.02) init through the converter
+    (bitwise against the oracle's RNE), then one fused-norm step with bf16 out."""
+    import torch
+    c = inputs.config_case("fp16_state")
+    B, NK, NV, D = c.B, c.NK, c.NV, c.D
+    say("fp16 state B=256")
+    st32 = dev(c.state)
+    st16 = g.gdn_state_f32_to_f16(st32)
+    ref16 = orc.f32_to_f16_bits(c.state)
+    got16 = host(st16)
+    assert np.array_equal(got16, ref16)
+    del st32
+    d = _dev_case(c)
+    y = g.gdn_decode_f16state(st16, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["z"],
+                              d["gn"], c.eps, out_dtype=torch.bfloat16, num_k_heads=NK,
+                              num_v_heads=NV)
+    heads = _sample_heads(B, NV, 600, 44)
+    ref_y = orc.decode(ref16, c.q, c.k, c.v, c.alpha, c.beta, B=B, NK=NK, NV=NV, Dk=D, Dv=D,
+                       z=c.z, gn=c.gn, eps=c.eps, state_kind=orc.STATE_F16, heads=heads)
+    got16, got_y = host(st16), host(y)
+    for (b, h) in heads:
+        sl = slice(h * D * D, (h + 1) * D * D)
+        gs = got16[b:b + 1, sl].view(np.float16).astype(np.float64)
+        rs = ref16[b:b + 1, sl].view(np.float16).astype(np.float64)
+        assert tile_err(gs, rs, 1, D) < TOL_F16, (b, h)
+        osl = slice(h * D, (h + 1) * D)
+        assert bf16_ok(got_y[b:b + 1, osl], ref_y[b:b + 1, osl], 1, D, TOL_F16) <= 1.0, (b, h)
+
+
+def test_fp16_state_padded_pitch_raw_and_f32(g):
+    """binary16 pool with a padded pitch (pads hold a canary pattern), raw o and
+    fp32 y outputs, several steps."""
+    import torch
+    B, NK, NV, D = 3, 2, 4, 64
+    c = inputs.make_case(45, B=B, NK=NK, NV=NV, D=D, T=1)
+    pitch = NV * D * D + 24
+    s16 = np.full((B, pitch), 0x7E01, np.uint16)
+    s16[:, :NV * D * D] = orc.f32_to_f16_bits(c.state)
+    st = dev(s16.view(np.float16))
+    ref = s16.copy()
+    d = _dev_case(c)
+    say("fp16 padded pitch")
+    for step in range(3):
+        o = g.gdn_decode_f16state(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                                  num_k_heads=NK, num_v_heads=NV, head_dim=D)
+        ref_o = orc.decode(ref, c.q, c.k, c.v, c.alpha, c.beta, B=B, NK=NK, NV=NV, Dk=D, Dv=D,
+                           state_kind=orc.STATE_F16)
+        assert out_err(host(o), ref_o, NV, D) < TOL_F16, step
+    y = g.gdn_decode_f16state(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["z"], d["gn"],
+                              c.eps, out_dtype=torch.float32, num_k_heads=NK, num_v_heads=NV)
+    ref_y = orc.decode(ref, c.q, c.k, c.v, c.alpha, c.beta, B=B, NK=NK, NV=NV, Dk=D, Dv=D, z=c.z,
+                       gn=c.gn, eps=c.eps, state_kind=orc.STATE_F16)
+    assert out_err(host(y), ref_y, NV, D) < TOL_F16
+    got = host(st)
+    assert (got[:, NV * D * D:] == 0x7E01).all()
+    assert tile_err(got[:, :NV * D * D].view(np.float16).astype(np.float64),
+                    ref[:, :NV * D * D].view(np.float16).astype(np.float64), NV, D) < TOL_F16
+
+
+# --------------------------------------------------------------------------- 5
+@pytest.mark.parametrize("init", ["zero", "normal"])
+def test_sequence_4096_tokens(g, init):
+    """B=4, T=4096, NV=48, NK=16, D=128: sampled heads through 4096 oracle steps
+    (every token's output and the final state)."""
+    c = inputs.config_case("sequence", state_init=init)
+    B, T, NK, NV, D = c.B, c.T, c.NK, c.NV, c.D
+    say("sequence", init, B, T)
+    d = _dev_case(c)
+    st = dev(c.state)
+    o = g.gdn_recurrence_seq(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"], seq_len=T,
+                             num_k_heads=NK, num_v_heads=NV, head_dim=D)
+    heads = _sample_heads(B, NV, 6, 55 if init == "zero" else 56)
+    ref_state = c.state.copy()
+    ref = orc.seq_head_threaded(ref_state, c.q, c.k, c.v, c.alpha, c.beta, B=B, T=T, NK=NK,
+                                NV=NV, Dk=D, Dv=D, heads=heads, threads=6)
+    got_o, got_s = host(o), host(st)
+    for (b, h) in heads:
+        rows = slice(b * T, (b + 1) * T)
+        osl = slice(h * D, (h + 1) * D)
+        assert out_err(got_o[rows, osl], ref[rows, osl], 1, D) < TOL_CHAIN, (b, h)
+        sl = slice(h * D * D, (h + 1) * D * D)
+        assert tile_err(got_s[b:b + 1, sl], ref_state[b:b + 1, sl], 1, D) < TOL_CHAIN, (b, h)
+
+
+def test_sequence_fused_norm_ragged(g):
+    """Sequence kernel with z (fused gated norm), a length that is not a multiple
+    of the staging chunk, every head."""
+    B, T, NK, NV, D = 2, 37, 16, 48, 128
+    c = inputs.make_case(57, B=B, NK=NK, NV=NV, D=D, T=T)
+    say("sequence norm ragged T=37")
+    d = _dev_case(c)
+    st = dev(c.state)
+    y = g.gdn_recurrence_seq(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["z"], d["gn"],
+                             c.eps, seq_len=T, num_k_heads=NK, num_v_heads=NV)
+    ref_state = c.state.copy()
+    ref = orc.seq(ref_state, c.q, c.k, c.v, c.alpha, c.beta, B=B, T=T, NK=NK, NV=NV, Dk=D, Dv=D,
+                  z=c.z, gn=c.gn, eps=c.eps)
+    assert out_err(host(y), ref, NV, D) < TOL_CHAIN
+    assert tile_err(host(st), ref_state, NV, D) < TOL_CHAIN
+
+
+def test_sequence_equals_chained_decode(g):
+    """T tokens in one sequence launch == T chained single-token launches (1e-4)."""
+    B, T, NK, NV, D = 3, 20, 4, 8, 128
+    c = inputs.make_case(58, B=B, NK=NK, NV=NV, D=D, T=T)
+    say("seq == chained decode")
+    d = _dev_case(c)
+    st_seq = dev(c.state)
+    o_seq = host(g.gdn_recurrence_seq(st_seq, d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                                      seq_len=T, num_k_heads=NK, num_v_heads=NV, head_dim=D))
+    st = dev(c.state)
+    o_chain = np.zeros_like(o_seq)
+    for t in range(T):
+        rows = [b * T + t for b in range(B)]
+        o_chain[rows] = host(g.gdn_decode(st, d["q"][rows], d["k"][rows], d["v"][rows],
+                                          d["alpha"][rows], d["beta"][rows], num_k_heads=NK,
+                                          num_v_heads=NV, head_dim=D))
+    assert out_err(o_seq, o_chain, NV, D) < TOL_CHAIN
+    assert tile_err(host(st_seq), host(st), NV, D) < TOL_CHAIN
+
+
+# ------------------------------------------------------------ dims and shapes
+@pytest.mark.parametrize("D", [4, 8, 16, 32, 64, 128, 256])
+@pytest.mark.parametrize("NV,NK", [(2, 2), (6, 2), (8, 4)])
+def test_every_head_dim_all_entry_points(g, D, NV, NK):
+    import torch
+    B, T = 3, 19
+    c = inputs.make_case(60 + D + NV, B=B, NK=NK, NV=NV, D=D, T=T)
+    say("dims", D, NV, NK)
+    d = _dev_case(c)
+    # decode (raw), decode_norm (fp32 and bf16), f16 twin on token 0 rows
+    rows = [b * T for b in range(B)]
+    c1 = inputs.make_case(60 + D + NV, B=B, NK=NK, NV=NV, D=D, T=1)
+    for kind in ("raw", "norm32", "norm16", "f16"):
+        if kind == "f16":
+            ref_state = orc.f32_to_f16_bits(c1.state)
+            st = dev(ref_state.view(np.float16))
+            ref = orc.decode(ref_state, c1.q, c1.k, c1.v, c1.alpha, c1.beta, B=B, NK=NK, NV=NV,
+                             Dk=D, Dv=D, z=c1.z, gn=c1.gn, eps=c1.eps, state_kind=orc.STATE_F16)
+            y = g.gdn_decode_f16state(st, dev(c1.q), dev(c1.k), dev(c1.v), dev(c1.alpha),
+                                      dev(c1.beta), dev(c1.z), dev(c1.gn), c1.eps,
+                                      out_dtype=torch.bfloat16, num_k_heads=NK, num_v_heads=NV)
+            assert bf16_ok(host(y), ref, NV, D, TOL_F16) <= 1.0
+            gs = host(st).view(np.float16).astype(np.float64)
+            assert tile_err(gs, ref_state.view(np.float16).astype(np.float64), NV, D) < TOL_F16
+            continue
+        ref_state = c1.state.copy()
+        norm = kind != "raw"
+        ref = orc.decode(ref_state, c1.q, c1.k, c1.v, c1.alpha, c1.beta, B=B, NK=NK, NV=NV, Dk=D,
+                         Dv=D, z=c1.z if norm else None, gn=c1.gn if norm else None, eps=c1.eps)
+        st = dev(c1.state)
+        if kind == "raw":
+            o = g.gdn_decode(st, dev(c1.q), dev(c1.k), dev(c1.v), dev(c1.alpha), dev(c1.beta),
+                             num_k_heads=NK, num_v_heads=NV, head_dim=D)
+            assert out_err(host(o), ref, NV, D) < TOL_STEP
+        else:
+            dt = torch.float32 if kind == "norm32" else torch.bfloat16
+            y = g.gdn_decode_norm(st, dev(c1.q), dev(c1.k), dev(c1.v), dev(c1.alpha),
+                                  dev(c1.beta), dev(c1.z), dev(c1.gn), c1.eps, out_dtype=dt,
+                                  num_k_heads=NK, num_v_heads=NV)
+            if dt == torch.float32:
+                assert out_err(host(y), ref, NV, D) < TOL_STEP
+            else:
+                assert bf16_ok(host(y), ref, NV, D, TOL_STEP) <= 1.0
+        assert tile_err(host(st), ref_state, NV, D) < TOL_STEP
+    del rows
+    # the sequence kernel, raw and normed, ragged T
+    for norm in (False, True):
+        ref_state = c.state.copy()
+        ref = orc.seq(ref_state, c.q, c.k, c.v, c.alpha, c.beta, B=B, T=T, NK=NK, NV=NV, Dk=D,
+                      Dv=D, z=c.z if norm else None, gn=c.gn if norm else None, eps=c.eps)
+        st = dev(c.state)
+        o = g.gdn_recurrence_seq(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                                 d["z"] if norm else None, d["gn"] if norm else None, c.eps,
+                                 seq_len=T, num_k_heads=NK, num_v_heads=NV, head_dim=D)
+        assert out_err(host(o), ref, NV, D) < TOL_CHAIN, norm
+        assert tile_err(host(st), ref_state, NV, D) < TOL_CHAIN, norm
+
+
+# ------------------------------------------------------------- special cases
+def test_pins_hold_on_gpu(g):
+    """The closed-form cases of the oracle pins, on the GPU kernels:
+    alpha=1/beta=0 leaves the state bit-identical; alpha=0/beta=1 writes v k^T;
+    one-hot keys with alpha=beta=1 store v in column h mod NK."""
+    B, NK, NV, D = 2, 4, 8, 128
+    c = inputs.make_case(61, B=B, NK=NK, NV=NV, D=D)
+    say("gpu pins")
+    ones = np.ones((B, NV), np.float32)
+    zeros = np.zeros((B, NV), np.float32)
+    st = dev(c.state)
+    g.gdn_decode(st, dev(c.q), dev(c.k), dev(c.v), dev(ones), dev(zeros), num_k_heads=NK,
+                 num_v_heads=NV, head_dim=D)
+    assert np.array_equal(host(st), c.state)
+    st = dev(c.state)
+    g.gdn_decode(st, dev(c.q), dev(c.k), dev(c.v), dev(zeros), dev(ones), num_k_heads=NK,
+                 num_v_heads=NV, head_dim=D)
+    got = host(st).reshape(B, NV, D, D)
+    for b in range(B):
+        for h in range(NV):
+            gk = c.k[b, (h % NK) * D:(h % NK + 1) * D]
+            want = np.outer(c.v[b, h * D:(h + 1) * D], gk).astype(np.float32)
+            assert np.array_equal(got[b, h], want), (b, h)
+    q = np.zeros((B, NK * D), np.float32)
+    for gg in range(NK):
+        q[:, gg * D + gg] = 1.0
+    v = np.repeat(np.arange(1, NV + 1, dtype=np.float32), D)[None, :].repeat(B, 0)
+    st = dev(np.zeros((B, NV * D * D), np.float32))
+    o = host(g.gdn_decode(st, dev(q), dev(q), dev(v), dev(ones), dev(ones), num_k_heads=NK,
+                          num_v_heads=NV, head_dim=D))
+    got = host(st).reshape(B, NV, D, D)
+    for h in range(NV):
+        want = np.zeros((D, D), np.float32)
+        want[:, h % NK] = h + 1
+        assert np.array_equal(got[0, h], want), h
+        np.testing.assert_allclose(o[0, h * D:(h + 1) * D], (h + 1) / np.sqrt(D), rtol=1e-6)
+
+
+def test_deterministic_bitwise(g):
+    """Two runs on the same inputs give the same bits (no atomics, fixed orders)."""
+    import torch
+    c = inputs.make_case(62, B=16, NK=16, NV=48, D=128, T=1)
+    say("determinism")
+    d = _dev_case(c)
+    outs = []
+    for _ in range(2):
+        st = dev(c.state)
+        y = g.gdn_decode_norm(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["z"], d["gn"],
+                              c.eps, out_dtype=torch.bfloat16, num_k_heads=16, num_v_heads=48)
+        outs.append((host(st).view(np.uint32), host(y)))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+
+
+def test_empty_batch_and_length_are_noops(g):
+    import torch
+    c = inputs.make_case(63, B=2, NK=2, NV=4, D=16, T=1)
+    say("empty")
+    d = _dev_case(c)
+    st = dev(c.state)
+    out = torch.full((2, 64), 7.0, device="cuda:0")
+    g.gdn_recurrence_seq(st, d["q"][:0], d["k"][:0], d["v"][:0], d["alpha"][:0], d["beta"][:0],
+                         out=out[:0], seq_len=0, num_k_heads=2, num_v_heads=4, head_dim=16)
+    e = torch.empty((0, 4 * 16 * 16), device="cuda:0")
+    o = g.gdn_decode(e, d["q"][:0], d["k"][:0], d["v"][:0], d["alpha"][:0], d["beta"][:0],
+                     num_k_heads=2, num_v_heads=4, head_dim=16)
+    assert o.shape[0] == 0
+    assert np.array_equal(host(st), c.state)
+    assert (host(out) == 7.0).all()
+
+
+def test_converters_bitwise(g):
+    """fp32 -> binary16 on special values, midpoints, subnormals and a random
+    sample, bitwise against the oracle's RNE; binary16 -> fp32 on all 65536
+    patterns; odd lengths exercise the scalar tail."""
+    import torch
+    r = np.random.Generator(np.random.PCG64(64))
+    h = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    f = h.view(np.float16).astype(np.float64)
+    nxt = np.concatenate([f[1:], [np.inf]])
+    mid = ((f + nxt) / 2)[np.isfinite(f) & np.isfinite(nxt)].astype(np.float32).view(np.uint32)
+    pats = [r.integers(0, 2 ** 32, size=1 << 22, dtype=np.uint64).astype(np.uint32)]
+    for base in (f[np.isfinite(f)].astype(np.float32).view(np.uint32), mid):
+        for dd in (-1, 0, 1):
+            pats.append((base.astype(np.int64) + dd).astype(np.uint32))
+    x = np.concatenate(pats).view(np.float32)
+    x = x[: x.size - (x.size % 8) + 5]          # an odd tail
+    say("converters", x.size)
+    got = host(g.gdn_state_f32_to_f16(dev(x)))
+    want = orc.f32_to_f16_bits(x)
+    nan = np.isnan(x)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert ((got[nan] & 0x7C00) == 0x7C00).all() and (got[nan] & 0x03FF).all()
+    hh = np.concatenate([h, h[:3]])
+    back = host(g.gdn_state_f16_to_f32(dev(hh.view(np.float16))))
+    ref = orc.f16_bits_to_f32(hh)
+    fin = ~np.isnan(ref)
+    assert np.array_equal(back[fin].view(np.uint32), ref[fin].view(np.uint32))
+    assert np.isnan(back[~fin]).all()
+    del torch
+
+
+def test_f16_state_keeps_subnormals(g):
+    """A state update whose results land in the binary16 subnormal range keeps
+    them (no flush to zero), matching the oracle bitwise for exact cases."""
+    B, NK, NV, D = 1, 1, 1, 16
+    c = inputs.make_case(65, B=B, NK=NK, NV=NV, D=D)
+    s16 = np.zeros((1, D * D), np.uint16)
+    s16[0, ::3] = 0x0001        # smallest subnormal
+    s16[0, 1::7] = 0x03FF       # largest subnormal
+    st = dev(s16.view(np.float16))
+    ones = np.ones((1, 1), np.float32)
+    zeros = np.zeros((1, 1), np.float32)
+    say("f16 subnormals")
+    g.gdn_decode_f16state(st, dev(c.q), dev(c.k), dev(c.v), dev(ones), dev(zeros),
+                          num_k_heads=NK, num_v_heads=NV, head_dim=D)
+    assert np.array_equal(host(st), s16)
+    half = np.full((1, 1), 0.5, np.float32)
+    g.gdn_decode_f16state(st, dev(c.q), dev(c.k), dev(c.v), dev(half), dev(zeros),
+                          num_k_heads=NK, num_v_heads=NV, head_dim=D)
+    ref = s16.copy()
+    orc.decode(ref, c.q, c.k, c.v, half, zeros, B=1, NK=1, NV=1, Dk=D, Dv=D,
+               state_kind=orc.STATE_F16)
+    assert np.array_equal(host(st), ref)
+    assert (ref[0, 1::7] == 0x0200).all()   # 0x03FF / 2 rounds to even 0x0200
+
+
+def test_validation_rejects_before_launch(g):
+    """Bad arguments come back as status codes and leave buffers untouched."""
+    import torch
+    c = inputs.make_case(66, B=2, NK=2, NV=4, D=16)
+    d = _dev_case(c)
+    st = dev(c.state)
+    say("validation")
+    out = d["v"].clone()
+    with pytest.raises(g.GdnError) as e:   # output aliases the state
+        g.gdn_decode(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"], out=st[:, :64],
+                     num_k_heads=2, num_v_heads=4, head_dim=16)
+    assert e.value.status == 5
+    with pytest.raises(g.GdnError) as e:   # unsupported head dim
+        g.gdn_decode(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"], num_k_heads=2,
+                     num_v_heads=4, head_dim=12)
+    with pytest.raises(g.GdnError) as e:   # NV not a multiple of NK
+        g.gdn_decode(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"], num_k_heads=2,
+                     num_v_heads=3, head_dim=16)
+    assert e.value.status == 2
+    mis = torch.zeros(2 * 32 + 1, device="cuda:0")[1:].view(2, 32)   # 4-byte offset
+    with pytest.raises(g.GdnError) as e:
+        g.gdn_decode(st, mis, mis, d["v"], d["alpha"], d["beta"], num_k_heads=2,
+                     num_v_heads=4, head_dim=16)
+    assert e.value.status == 3
+    with pytest.raises(g.GdnError) as e:   # negative eps
+        g.gdn_decode_norm(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["z"], d["gn"],
+                          -1.0, num_k_heads=2, num_v_heads=4)
+    assert e.value.status == 8
+    src = torch.zeros(64, device="cuda:0")
+    with pytest.raises(g.GdnError) as e:   # converter in place
+        g.gdn_state_f32_to_f16(src, src.view(torch.float16)[:64])
+    assert e.value.status == 5
+    assert np.array_equal(host(st), c.state)
+    assert np.array_equal(host(out), c.v)
