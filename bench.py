@@ -157,7 +157,7 @@ def run_seq(g, calls: int):
         g.gdn_recurrence_seq(st, t["q"], t["k"], t["v"], t["alpha"], t["beta"], out=out, seq_len=T,
                              num_k_heads=NK, num_v_heads=NV, head_dim=D)
 
-    ms = _timed(step, calls, 1)
+    ms = _timed(step, calls, 3)
     flops = 7.0 * D * D * B * NV * T
     byts = B * T * (2 * NK * D * 4 + NV * (D * 4 + 8 + D * 4)) + 2.0 * B * NV * D * D * 4
     del t, st, out
@@ -278,7 +278,10 @@ def main():
     ap.add_argument("--pools", type=int, default=48)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-extra", action="store_true", help="main workload only")
+    ap.add_argument("--extras", default="fp16_state,sequence,real_head",
+                    help="comma list of extra workloads: fp16_state, sequence, real_head")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--seq-only", action="store_true", help="time the sequence workload alone")
     ap.add_argument("--pmc-run", action="store_true",
                     help="copy-kernel calibration + main step only (for rocprofv3 --pmc)")
     args = ap.parse_args()
@@ -299,6 +302,9 @@ def main():
     if args.pmc_run:
         calibrate_and_profile(g, args.steps)
         return
+    if args.seq_only:
+        print(json.dumps(run_seq(g, 5)), flush=True)
+        return
 
     m = run_main(g, args.steps, args.warmup, args.pools)
     ms = m["ms"]
@@ -309,10 +315,11 @@ def main():
         "ms_per_call": round(m["ms_hot"], 5),
         "state_GBps": round(m["state_bytes"] / m["ms_hot"] / 1e6, 1),
         "note": "same pool every call: the 201 MB state can stay in the 256 MB Infinity Cache"}}
-    if not args.no_extra:
-        extra["fp16_state"] = run_fp16(g, 100)
-        extra["sequence"] = run_seq(g, 3)
-        extra["real_head"] = run_real_head(g, 50)
+    wanted = [] if args.no_extra else [w for w in args.extras.split(",") if w]
+    runners = {"fp16_state": lambda: run_fp16(g, 100), "sequence": lambda: run_seq(g, 5),
+               "real_head": lambda: run_real_head(g, 50)}
+    for w in wanted:
+        extra[w] = runners[w]()
     cpu = None if args.no_cpu else cpu_baseline(args.cpu_seconds)
     line = {
         "metric": "GDN decode state GB/s and % HBM roofline; tokens/s·batch at HV=48,D=128",
