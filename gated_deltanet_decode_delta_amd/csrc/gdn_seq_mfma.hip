@@ -1,0 +1,396 @@
+// gdn_seq_mfma.hip -- the T-token recurrence at D = 128 on the fp32 matrix cores.
+//
+// Same operation as the register-resident token loop of gdn_seq.hip (metrale
+// "layers/ops/ssm_gdn_a.rs", `gdn_prefill_regresident`; the update of
+// logicaffeine "codegen_cuda/gdn.rs", `gdn_step`), evaluated C = 16 tokens at a
+// time so that the state contractions become 16x16x4 fp32 MFMA products.
+// Within a chunk, with M[t][s] = alpha_{s+1} ... alpha_t (M[t][t] = 1),
+// P_t = alpha_0 ... alpha_t and S0 the state at the chunk start, unrolling
+// S_t = alpha_t S_{t-1} + c_t k_t^T gives
+//     c_t + sum_{s<t} beta_t M[t][s] (k_s.k_t) c_s = beta_t (v_t - P_t S0 k_t)
+//     o_t = P_t S0 q_t + sum_{s<=t} M[t][s] (k_s.q_t) c_s
+//     S_end = P_15 S0 + sum_s M[15][s] c_s k_s^T
+// so per chunk: U = S0 K^T and W = S0 Q^T (MFMA), the 16x16 unit lower
+// triangular system (I + A) (its inverse T by forward substitution on the
+// vector ALU), C = R T^T with R = beta (V - P U) (MFMA), O = P W + C G^T (MFMA)
+// and S <- P_15 S + (C diag(M[15][.])) K (MFMA).  The range products M are
+// formed directly (no division by a running product), so any alpha >= 0 works,
+// including alpha = 0.  Rounding differs from the token loop by reordering
+// only; both are checked against the same fp64 oracle.
+//
+// Mapping.  One workgroup of eight waves per (sequence, value head), two per
+// SIMD, so that one wave's vector-ALU work (the 16x16 solve, the scalars)
+// overlaps the other's matrix-core work; wave w owns state rows [16w, 16w+16).
+// The state lives in the MFMA accumulator layout transposed: register r of
+// tile m of lane l holds S[16w + l%16][16m + 4(l/16) + r].  That is exactly the
+// B-operand layout of the product K S^T with the contraction index j ordered
+// (m, r, l/16), so the state never moves between the U/W products and the
+// update.  k, q and k^T of the chunk are staged in LDS (read once per 16-row
+// tile instead of once per lane); v and z go from global memory straight to the
+// lanes that use them.
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kD = 128;
+constexpr int kC = 16;           // tokens per chunk
+constexpr int kWaves = 8;        // wave w owns state rows [16w, 16w + 16)
+constexpr int kThreads = 64 * kWaves;
+constexpr int kKS = kD + 4;      // row stride (floats) of k_s / q_s
+constexpr int kTS = kC + 4;      // row stride of kt_s and of the per-wave 16x16 matrices
+constexpr int kPieces = kC * kD / 4 / kThreads;   // 16-byte pieces of a chunk's k (or q) per thread
+constexpr int kPartWaves = 4;    // waves forming the chunk's k.k / k.q (two 16-column slices each)
+static_assert(kPieces * kThreads * 4 == kC * kD, "staging covers the chunk exactly");
+
+__device__ __forceinline__ f32x4 mfma(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// inclusive prefix / suffix products over one 16-lane DPP row
+__device__ __forceinline__ float dpp_mul(float x, int ctrl_sel) {
+    int r;
+    switch (ctrl_sel) {
+        case 0: r = __builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(x), 0x111, 0xF, 0xF, false); break;
+        case 1: r = __builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(x), 0x112, 0xF, 0xF, false); break;
+        case 2: r = __builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(x), 0x114, 0xF, 0xF, false); break;
+        case 3: r = __builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(x), 0x118, 0xF, 0xF, false); break;
+        case 4: r = __builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(x), 0x101, 0xF, 0xF, false); break;
+        case 5: r = __builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(x), 0x102, 0xF, 0xF, false); break;
+        case 6: r = __builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(x), 0x104, 0xF, 0xF, false); break;
+        default: r = __builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(x), 0x108, 0xF, 0xF, false); break;
+    }
+    return __int_as_float(r);
+}
+
+}  // namespace
+
+template <bool NORM>
+__global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
+    __shared__ __align__(16) float k_s[kC * kKS], q_s[kC * kKS];
+    __shared__ __align__(16) float kt_s[kD * kTS];
+    __shared__ f32x4 part_s[kPartWaves][2][64];          // partial k.k and k.q tiles
+    __shared__ __align__(16) float a_s[kC * kTS], t_s[kC * kTS];  // A and T = (I + A)^{-1}
+    __shared__ __align__(16) float m_s[kC * kTS], mt_s[kC * kTS]; // M[t][s] and its transpose
+    __shared__ __align__(16) float al_s[kC], be_s[kC], p_s[kC], d_s[kC];
+    __shared__ float nrm_s[NORM ? kWaves : 1][kC];
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6, l = tid & 63, g = l >> 4, li = l & 15;
+    const int head = blockIdx.x;
+    const int b = head / a.nv;
+    const int h = head - b * a.nv;
+    const int kh = h % a.nk;  // tiled key-head pairing
+    const int T = a.seq_len;
+    const int64_t row_base = (int64_t)b * T;
+    float *slot = static_cast<float *>(a.state) + (int64_t)b * a.pitch + (int64_t)h * (kD * kD);
+    const int64_t vcol = (int64_t)h * kD + 16 * w + li;   // this lane's v / z / output column
+
+    // Stored state: the true state is gam * S, with S[m][r] holding
+    // S[row 16w + li][col 16m + 4g + r].  Keeping the chunk decays in the scalar
+    // gam leaves S to the matrix cores alone.
+    const int row = 16 * w + li;
+    f32x4 S[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+        S[m] = *reinterpret_cast<const f32x4 *>(slot + (int64_t)row * kD + 16 * m + 4 * g);
+    float gam = 1.0f;
+    const float gnv = NORM ? a.gn[row] : 0.0f;
+
+    // prefetch registers for one chunk: 16-byte pieces f = tid + 256u of the
+    // chunk's k and q ([16][128]); v (and z) of the lane's own (t, i) entries
+    float4 pk[kPieces], pq[kPieces];
+    float pv[4], pz[4];
+    float pal = 1.0f, pbe = 0.0f;
+    auto prefetch = [&](int t0) {
+        // Padding tokens (past T): alpha 1, beta 0 and zero k/q/v leave the
+        // state and every real token unchanged.  Their loads read row T-1
+        // (always valid) and are zeroed by a select, so no load is predicated.
+        const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int u = 0; u < kPieces; ++u) {
+            const int f = tid + kThreads * u;     // < kC * kD / 4
+            const int t = f >> 5, col = (f & 31) * 4;
+            const bool ok = t0 + t < T;
+            const int64_t rr = row_base + (ok ? t0 + t : T - 1);
+            const int64_t off = rr * a.qk_stride + (int64_t)kh * kD + col;
+            const float4 kx = *reinterpret_cast<const float4 *>(a.k + off);
+            const float4 qx = *reinterpret_cast<const float4 *>(a.q + off);
+            pk[u] = ok ? kx : zero;
+            pq[u] = ok ? qx : zero;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 4 * g + r;
+            const bool ok = t0 + t < T;
+            const int64_t rr = row_base + (ok ? t0 + t : T - 1);
+            const float vx = a.v[rr * a.v_stride + vcol];
+            pv[r] = ok ? vx : 0.f;
+            if constexpr (NORM) {
+                const float zx = a.z[rr * a.z_stride + vcol];
+                pz[r] = ok ? zx : 0.f;
+            } else {
+                pz[r] = 0.f;
+            }
+        }
+        pal = 1.0f;
+        pbe = 0.0f;
+        if (tid < kC && t0 + tid < T) {
+            const int64_t rr = row_base + t0 + tid;
+            pal = a.alpha[rr * a.ab_stride + h];
+            pbe = a.beta[rr * a.ab_stride + h];
+        }
+    };
+    auto stage = [&]() {
+#pragma unroll
+        for (int u = 0; u < kPieces; ++u) {
+            const int f = tid + kThreads * u;
+            const int t = f >> 5, col = (f & 31) * 4;
+            *reinterpret_cast<float4 *>(&k_s[t * kKS + col]) = pk[u];
+            *reinterpret_cast<float4 *>(&q_s[t * kKS + col]) = pq[u];
+            kt_s[(col + 0) * kTS + t] = pk[u].x;
+            kt_s[(col + 1) * kTS + t] = pk[u].y;
+            kt_s[(col + 2) * kTS + t] = pk[u].z;
+            kt_s[(col + 3) * kTS + t] = pk[u].w;
+        }
+        if (tid < kC) {   // lanes 0..15 of wave 0: one DPP row
+            al_s[tid] = pal;
+            be_s[tid] = pbe;
+            float pre = pal;   // P_t = alpha_0 ... alpha_t
+            pre *= dpp_mul(pre, 0);
+            pre *= dpp_mul(pre, 1);
+            pre *= dpp_mul(pre, 2);
+            pre *= dpp_mul(pre, 3);
+            p_s[tid] = pre;
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            // lane s: column s of the range products M[t][s] = alpha_{s+1} ... alpha_t
+            f32x4 alv[4];
+#pragma unroll
+            for (int x4 = 0; x4 < 4; ++x4) alv[x4] = *reinterpret_cast<const f32x4 *>(&al_s[4 * x4]);
+            const int s = tid;
+            float mts = 1.0f;
+#pragma unroll
+            for (int t = 0; t < kC; ++t) {
+                if (t > s) mts *= alv[t >> 2][t & 3];
+                const float v = t >= s ? mts : 0.0f;
+                m_s[t * kTS + s] = v;
+                mt_s[s * kTS + t] = v;
+            }
+            d_s[s] = mts;   // M[15][s]
+        }
+    };
+
+    // waves 0..3 (one per SIMD) form a quarter each of the chunk's k.k and k.q
+    // products (columns 32w .. 32w + 31); the quarters are summed when read
+    auto partials = [&]() {
+        if (w < kPartWaves) {
+            f32x4 KK = f32x4{0.f, 0.f, 0.f, 0.f}, KQ = KK;
+#pragma unroll
+            for (int mm = 0; mm < 2; ++mm) {
+                const int m = 2 * w + mm;
+                const f32x4 ka = *reinterpret_cast<const f32x4 *>(&k_s[li * kKS + 16 * m + 4 * g]);
+                const f32x4 qa = *reinterpret_cast<const f32x4 *>(&q_s[li * kKS + 16 * m + 4 * g]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    KK = mfma(ka[r], ka[r], KK);   // k_t . k_s
+                    KQ = mfma(ka[r], qa[r], KQ);   // k_t . q_s
+                }
+            }
+            part_s[w][0][l] = KK;
+            part_s[w][1][l] = KQ;
+        }
+    };
+
+    float vcur[4], zcur[4];
+    prefetch(0);
+    stage();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        vcur[r] = pv[r];
+        zcur[r] = pz[r];
+    }
+    // drain every load (the state included) so that no conservative vmcnt wait
+    // lands inside the chunk loop, where it would also wait for the prefetch
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    partials();
+    __syncthreads();
+
+    float *outp = static_cast<float *>(a.out);
+    for (int t0 = 0; t0 < T; t0 += kC) {
+        const bool has_next = t0 + kC < T;
+        const int nt = T - t0 < kC ? T - t0 : kC;
+        if (has_next) prefetch(t0 + kC);
+
+        // Lane (g, li) owns tile entries (a, b) = (4g + r, li):
+        //   A[a][b] = beta_a M[a][b] (k_a.k_b)  for b < a  (tile layout, for the solve)
+        //   G[b][a] = M[b][a] (q_b.k_a)          for a <= b (MFMA A-operand layout)
+        // k.k is symmetric and k_a.q_b is the tile entry of the k.q product, so
+        // no value moves between lanes.  Every wave forms its own G; wave 0 also
+        // forms A and solves T = (I + A)^{-1} once for the workgroup (lane column
+        // c = li, forward substitution), while the other waves start on U and W.
+        const f32x4 bet = *reinterpret_cast<const f32x4 *>(&be_s[4 * g]);
+        const f32x4 mA = *reinterpret_cast<const f32x4 *>(&mt_s[li * kTS + 4 * g]);   // M[4g+r][li]
+        const f32x4 mG = *reinterpret_cast<const f32x4 *>(&m_s[li * kTS + 4 * g]);    // M[li][4g+r]
+        f32x4 Ga;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float kq = 0.f;
+#pragma unroll
+            for (int v2 = 0; v2 < kPartWaves; ++v2) kq += part_s[v2][1][l][r];
+            Ga[r] = mG[r] * kq;   // M[li][a] is 0 above the diagonal
+        }
+        if (w == 0) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int ai = 4 * g + r;
+                float kk = 0.f;
+#pragma unroll
+                for (int v2 = 0; v2 < kPartWaves; ++v2) kk += part_s[v2][0][l][r];
+                a_s[ai * kTS + li] = li < ai ? bet[r] * mA[r] * kk : 0.0f;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            float x[kC];
+#pragma unroll
+            for (int t = 0; t < kC; ++t) x[t] = 0.0f;
+#pragma unroll
+            for (int t = 0; t < kC; ++t) {
+                float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+                for (int s4 = 0; s4 < (t + 3) / 4; ++s4) {
+                    const f32x4 av = *reinterpret_cast<const f32x4 *>(&a_s[t * kTS + 4 * s4]);
+                    acc0 = fmaf(av[0], x[4 * s4 + 0], acc0);
+                    acc1 = fmaf(av[1], x[4 * s4 + 1], acc1);
+                    acc0 = fmaf(av[2], x[4 * s4 + 2], acc0);
+                    acc1 = fmaf(av[3], x[4 * s4 + 3], acc1);
+                }
+                x[t] = t < li ? 0.0f : (t == li ? 1.0f : -(acc0 + acc1));
+            }
+            if (g == 0) {
+#pragma unroll
+                for (int t = 0; t < kC; ++t) t_s[t * kTS + li] = x[t];
+            }
+        }
+
+        // U^T = K S^T and W^T = Q S^T on the matrix cores
+        f32x4 U = f32x4{0.f, 0.f, 0.f, 0.f}, W = U;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const f32x4 ka = *reinterpret_cast<const f32x4 *>(&k_s[li * kKS + 16 * m + 4 * g]);
+            const f32x4 qa = *reinterpret_cast<const f32x4 *>(&q_s[li * kKS + 16 * m + 4 * g]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                U = mfma(ka[r], S[m][r], U);
+                W = mfma(qa[r], S[m][r], W);
+            }
+        }
+        __syncthreads();   // T visible to every wave
+
+        const f32x4 Ta = *reinterpret_cast<const f32x4 *>(&t_s[li * kTS + 4 * g]);
+        const f32x4 Pt = *reinterpret_cast<const f32x4 *>(&p_s[4 * g]);
+        const f32x4 Dt = *reinterpret_cast<const f32x4 *>(&d_s[4 * g]);
+        const float Plast = p_s[kC - 1];
+
+        // R = beta (v - P gam U);  C' = T R;  O = P gam W + G C'
+        f32x4 R, Cp, O;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float pg = Pt[r] * gam;
+            R[r] = bet[r] * (vcur[r] - pg * U[r]);
+            O[r] = pg * W[r];
+        }
+        Cp = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) Cp = mfma(Ta[s4], R[s4], Cp);
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) O = mfma(Ga[s4], Cp[s4], O);
+        if constexpr (!NORM) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * g + r;
+                if (t < nt) outp[(row_base + t0 + t) * a.out_stride + vcol] = O[r] * a.scale;
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float o = O[r] * a.scale;
+                const float ss = group_sum<16>(o * o);
+                if (li == 0) nrm_s[w][4 * g + r] = ss;
+            }
+            __syncthreads();   // per-wave sums of o^2 visible
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * g + r;
+                float tot = 0.f;
+#pragma unroll
+                for (int v2 = 0; v2 < kWaves; ++v2) tot += nrm_s[v2][t];
+                const float rr_ = sqrtf(tot * (1.0f / kD) + a.eps);
+                if (t < nt) {
+                    const float o = O[r] * a.scale;
+                    outp[(row_base + t0 + t) * a.out_stride + vcol] = (gnv * o / rr_) * silu(zcur[r]);
+                }
+            }
+        }
+
+        // true state: gam S -> P_15 gam S + K^T (C' diag(M[15][.]))^T.  Keep the
+        // decay in gam (S += K^T (C' M[15][.] / gam')^T) while gam' stays in
+        // [2^-60, 2^60]; otherwise fold it into S first (strong forgetting).
+        float gnew = gam * Plast;
+        float cscale;
+        if (gnew >= 0x1p-60f && gnew <= 0x1p60f) {
+            cscale = 1.0f / gnew;
+        } else {
+            const float f = gnew;
+#pragma unroll
+            for (int m = 0; m < 8; ++m) S[m] *= f;
+            gnew = 1.0f;
+            cscale = 1.0f;
+        }
+        gam = gnew;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Cp[r] *= Dt[r] * cscale;
+        f32x4 kta[8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) kta[m] = *reinterpret_cast<const f32x4 *>(&kt_s[(16 * m + li) * kTS + 4 * g]);
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+            for (int m = 0; m < 8; ++m) S[m] = mfma(kta[m][s4], Cp[s4], S[m]);
+
+        __syncthreads();   // every read of this chunk's staged data is done
+        if (has_next) {
+            stage();
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                vcur[r] = pv[r];
+                zcur[r] = pz[r];
+            }
+            __syncthreads();   // next chunk staged
+            partials();
+            __syncthreads();   // its k.k / k.q partial tiles visible
+        }
+    }
+
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+        *reinterpret_cast<f32x4 *>(slot + (int64_t)row * kD + 16 * m + 4 * g) = S[m] * gam;
+}
+
+hipError_t launch_seq_mfma(const StepArgs &a, OutMode mode, hipStream_t stream) {
+    const unsigned grid = (unsigned)((int64_t)a.batch * a.nv);
+    if (mode == kOutRawF32)
+        hipLaunchKernelGGL(seq_mfma_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, a);
+    else if (mode == kOutNormF32)
+        hipLaunchKernelGGL(seq_mfma_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, a);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace gdn
