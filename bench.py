@@ -168,6 +168,55 @@ def run_seq(g, calls: int):
             "GBps": round(byts / ms / 1e6, 1), "tokens_per_s": round(B * T / ms * 1e3, 1)}
 
 
+def run_verify(g, calls: int, pools: int = 16):
+    """Draft verification on the decode shapes: T tokens per sequence in one
+    launch (state read once, T-1 rollback tiles and the final state written),
+    against T chained single-token calls on the same pools."""
+    import torch
+    from gated_deltanet_decode_delta_amd import inputs
+
+    B, NK, NV, D, pitch = 64, 16, 48, 128, 983040
+    dev = "cuda:0"
+    res = {"workload": "draft verify, B=64, NV=48, NK=16, D=128, fused norm fp32, padded pool"}
+    for T in (2, 4):
+        log(f"[bench] verify: B={B} T={T} pools={pools}")
+        c = inputs.make_case(3100 + T, B=B, NK=NK, NV=NV, D=D, T=T, pitch=pitch)
+        st0 = torch.from_numpy(c.state).to(dev)
+        states = [st0.clone() for _ in range(pools)]
+        del st0
+        t = {n: torch.from_numpy(getattr(c, n)).to(dev) for n in ("q", "k", "v", "z", "alpha", "beta", "gn")}
+        inters = [torch.empty((B * (T - 1), NV * D * D), device=dev) for _ in range(pools)]
+        out = torch.empty((B * T, NV * D), device=dev)
+        rows = [torch.arange(B, device=dev) * T + j for j in range(T)]
+        per_tok = [{n: t[n][r].contiguous() for n in ("q", "k", "v", "z", "alpha", "beta")} for r in rows]
+        out1 = torch.empty((B, NV * D), device=dev)
+
+        def step(i):
+            p = i % pools
+            g.gdn_decode_verify(states[p], t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["z"],
+                                t["gn"], 1e-6, out=out, inter_state=inters[p], num_tokens=T,
+                                num_k_heads=NK, num_v_heads=NV)
+
+        def chained(i):
+            p = i % pools
+            for j in range(T):
+                x = per_tok[j]
+                g.gdn_decode_norm(states[p], x["q"], x["k"], x["v"], x["alpha"], x["beta"], x["z"],
+                                  t["gn"], 1e-6, out=out1, num_k_heads=NK, num_v_heads=NV)
+
+        ms = _timed(step, calls, 5)
+        ms_chain = _timed(chained, calls, 5)
+        tile = NV * D * D * 4.0
+        algo = B * (T + 1) * tile + B * T * NV * (head_bytes(D, NV, NK, 4, 4, True) - 2 * D * D * 4)
+        res[f"T{T}"] = {"ms_per_call": round(ms, 5), "hbm_GBps_algorithmic": round(algo / ms / 1e6, 1),
+                        "hbm_frac_algorithmic": round(algo / ms / 1e6 / HBM_PEAK_GBS, 4),
+                        "chained_decode_ms": round(ms_chain, 5),
+                        "speedup_vs_chained": round(ms_chain / ms, 3)}
+        del states, inters, t, out, per_tok, out1
+        torch.cuda.empty_cache()
+    return res
+
+
 def run_real_head(g, tokens: int):
     import torch
     from gated_deltanet_decode_delta_amd import inputs
@@ -270,6 +319,64 @@ def calibrate_and_profile(g, steps: int):
     run_main(g, steps, 2, 48)
 
 
+def pmc_summarize(fetch_csv: str, write_csv: str):
+    """Turn the two rocprofv3 --pmc counter files of a --pmc-run (FETCH_SIZE,
+    then WRITE_SIZE, KiB per dispatch) into the committed traffic record: each
+    counter is scaled by what it reads for the 1 GiB device copy, whose bytes
+    are known."""
+    import csv
+    import statistics
+
+    def per_kernel(path, counter):
+        vals = {}
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    name = "void gdn::decode_kernel<128, float, 1>(gdn::StepArgs)"
+    copy = "__amd_rocclr_copyBuffer"
+    nbytes = float(1 << 30)
+    # the 1 GiB copy is the largest copy dispatch of the run (torch's set-up
+    # copies of the inputs use the same kernel on smaller buffers)
+    cf, cw = max(fetch[copy]), max(write[copy])
+    ff, wf = nbytes / (cf * 1024), nbytes / (cw * 1024)
+    kf, kw = statistics.mean(fetch[name]), statistics.mean(write[name])
+    from gated_deltanet_decode_delta_amd import inputs
+    cfg = inputs.CONFIGS["batched"]
+    algo = cfg["B"] * cfg["NV"] * head_bytes(cfg["D"], cfg["NV"], cfg["NK"], 4, 4, True)
+    rec = {
+        "kernel": name,
+        "workload": "gdn_decode_norm, B=64, NV=48, NK=16, D=128, fp32 state, pitch 983040, fp32 out",
+        "kernel_hash": kernel_hash(),
+        "kernel_sources": list(KERNEL_SOURCES),
+        "dispatches": min(len(fetch[name]), len(write[name])),
+        "fetch_size_kib_per_dispatch": round(kf, 1),
+        "write_size_kib_per_dispatch": round(kw, 1),
+        "calibration": {"kernel": copy + " (torch copy_ of a 1 GiB fp32 buffer)",
+                        "bytes_read": int(nbytes), "bytes_written": int(nbytes),
+                        "fetch_size_kib": round(cf, 1), "write_size_kib": round(cw, 1),
+                        "fetch_factor": round(ff, 5), "write_factor": round(wf, 5)},
+        "fetch_bytes_per_launch": int(kf * 1024 * ff),
+        "write_bytes_per_launch": int(kw * 1024 * wf),
+        "bytes_per_launch": int(kf * 1024 * ff + kw * 1024 * wf),
+        "algorithmic_bytes_per_launch": int(algo),
+        "commands": [
+            "cd /tmp && TMPDIR=/tmp timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE -d <out>/fetch -o fetch "
+            "--output-format csv -- python3 <repo>/bench.py --pmc-run --steps 20",
+            "cd /tmp && TMPDIR=/tmp timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE -d <out>/write -o write "
+            "--output-format csv -- python3 <repo>/bench.py --pmc-run --steps 20",
+            "python3 <repo>/bench.py --pmc-summarize <out>/fetch/fetch_counter_collection.csv "
+            "<out>/write/write_counter_collection.csv"],
+    }
+    with open(PMC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps({"bytes_per_launch": rec["bytes_per_launch"], "algorithmic": rec["algorithmic_bytes_per_launch"]}))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -278,14 +385,19 @@ def main():
     ap.add_argument("--pools", type=int, default=48)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-extra", action="store_true", help="main workload only")
-    ap.add_argument("--extras", default="fp16_state,sequence,real_head",
-                    help="comma list of extra workloads: fp16_state, sequence, real_head")
+    ap.add_argument("--extras", default="fp16_state,sequence,verify,real_head",
+                    help="comma list of extra workloads: fp16_state, sequence, verify, real_head")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--seq-only", action="store_true", help="time the sequence workload alone")
+    ap.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the traffic record from two rocprofv3 --pmc counter files (no GPU)")
     ap.add_argument("--pmc-run", action="store_true",
                     help="copy-kernel calibration + main step only (for rocprofv3 --pmc)")
     args = ap.parse_args()
 
+    if args.pmc_summarize:
+        pmc_summarize(*args.pmc_summarize)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -317,7 +429,7 @@ def main():
         "note": "same pool every call: the 201 MB state can stay in the 256 MB Infinity Cache"}}
     wanted = [] if args.no_extra else [w for w in args.extras.split(",") if w]
     runners = {"fp16_state": lambda: run_fp16(g, 100), "sequence": lambda: run_seq(g, 5),
-               "real_head": lambda: run_real_head(g, 50)}
+               "verify": lambda: run_verify(g, 100), "real_head": lambda: run_real_head(g, 50)}
     for w in wanted:
         extra[w] = runners[w]()
     cpu = None if args.no_cpu else cpu_baseline(args.cpu_seconds)

@@ -35,8 +35,9 @@ STATUS_NAMES = {
     8: "GDN_ERR_ARG",
 }
 EXPORTS = ("gdn_decode", "gdn_decode_norm", "gdn_decode_f16state", "gdn_recurrence_seq",
-           "gdn_state_f32_to_f16", "gdn_state_f16_to_f32", "gdn_status_string",
-           "gdn_last_hip_error")
+           "gdn_decode_verify", "gdn_state_f32_to_f16", "gdn_state_f16_to_f32",
+           "gdn_status_string", "gdn_last_hip_error")
+VERIFY_MAX_TOKENS = 8
 
 
 class GdnError(RuntimeError):
@@ -69,10 +70,12 @@ def _lib():
     lib.gdn_decode_f16state.argtypes = norm_sig
     lib.gdn_recurrence_seq.argtypes = [vp, i64, vp, vp, i64, vp, i64, vp, vp, i64, vp, i64, vp,
                                        f32, vp, i64, i32, i32, i32, i32, i32, i32, vp]
+    lib.gdn_decode_verify.argtypes = [vp, i64, vp, i64, vp, vp, i64, vp, i64, vp, vp, i64, vp, i64,
+                                      vp, f32, vp, i64, i32, i32, i32, i32, i32, i32, vp]
     lib.gdn_state_f32_to_f16.argtypes = [vp, vp, i64, vp]
     lib.gdn_state_f16_to_f32.argtypes = [vp, vp, i64, vp]
     for name in ("gdn_decode", "gdn_decode_norm", "gdn_decode_f16state", "gdn_recurrence_seq",
-                 "gdn_state_f32_to_f16", "gdn_state_f16_to_f32"):
+                 "gdn_decode_verify", "gdn_state_f32_to_f16", "gdn_state_f16_to_f32"):
         getattr(lib, name).restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
@@ -270,6 +273,50 @@ def gdn_recurrence_seq(state, q, k, v, alpha, beta, z=None, norm_weight=None, ep
                                      float(eps), op, os_, B, T, NK, NV, D, D,
                                      _stream(state, stream)), "gdn_recurrence_seq")
     return out
+
+
+def gdn_decode_verify(state, q, k, v, alpha, beta, z=None, norm_weight=None, eps: float = 1e-6,
+                      out=None, inter_state=None, *, num_tokens: int, num_k_heads: int,
+                      num_v_heads: int, head_dim: Optional[int] = None, stream=None):
+    """``num_tokens`` tokens per sequence in one launch; returns ``(out, inter_state)``.
+
+    ``inter_state`` (allocated when not given, fp32 ``[B*(num_tokens-1), pitch]``)
+    receives the state after each token but the last, slot ``b*(num_tokens-1)+t``."""
+    torch = _torch()
+    B = state.shape[0]
+    T = int(num_tokens)
+    NK, NV, D = _dims(norm_weight, num_k_heads, num_v_heads, head_dim)
+    rows = B * T
+    if out is None:
+        out = _empty_rows(rows, NV * D, torch.float32, state)
+    if inter_state is None and T > 1:
+        inter_state = torch.empty((B * (T - 1), NV * D * D), dtype=torch.float32, device=state.device)
+    sp, pitch = _state(state, B, NV * D * D, torch.float32)
+    if T > 1:
+        ip, ipitch = _state(inter_state, B * (T - 1), NV * D * D, torch.float32)
+    else:
+        ip, ipitch = None, 0
+    qp, qs, _ = _rows(q, rows, NK * D, "q", torch.float32)
+    kp, ks, _ = _rows(k, rows, NK * D, "k", torch.float32)
+    if qs != ks:
+        raise ValueError("q and k must share one row stride")
+    vp_, vs, _ = _rows(v, rows, NV * D, "v", torch.float32)
+    ap, abs_, _ = _rows(alpha, rows, NV, "alpha", torch.float32)
+    bp, bs, _ = _rows(beta, rows, NV, "beta", torch.float32)
+    if abs_ != bs:
+        raise ValueError("alpha and beta must share one row stride")
+    if z is not None:
+        zp, zs, _ = _rows(z, rows, NV * D, "z", torch.float32)
+        if norm_weight is None or norm_weight.dtype != torch.float32:
+            raise ValueError("norm_weight must be fp32 [D]")
+        gp = norm_weight.data_ptr()
+    else:
+        zp, zs, gp = None, 0, None
+    op, os_, _ = _rows(out, rows, NV * D, "out", torch.float32)
+    _check(_lib().gdn_decode_verify(sp, pitch, ip, ipitch, qp, kp, qs, vp_, vs, ap, bp, abs_, zp, zs,
+                                    gp, float(eps), op, os_, B, T, NK, NV, D, D,
+                                    _stream(state, stream)), "gdn_decode_verify")
+    return out, inter_state
 
 
 def gdn_state_f32_to_f16(src, dst=None, stream=None):

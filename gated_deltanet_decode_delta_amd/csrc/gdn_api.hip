@@ -223,6 +223,47 @@ gdn_status gdn_recurrence_seq(float *state, int64_t state_seq_stride, const floa
                                   norm ? gdn::kOutNormF32 : gdn::kOutRawF32, (hipStream_t)stream));
 }
 
+gdn_status gdn_decode_verify(float *state, int64_t state_seq_stride, float *inter_state,
+                             int64_t inter_pitch, const float *q, const float *k, int64_t qk_stride,
+                             const float *v, int64_t v_stride, const float *alpha, const float *beta,
+                             int64_t ab_stride, const float *z, int64_t z_stride,
+                             const float *norm_weight, float eps, float *out, int64_t out_stride,
+                             int32_t batch, int32_t num_tokens, int32_t num_k_heads,
+                             int32_t num_v_heads, int32_t k_dim, int32_t v_dim, void *stream) {
+    const bool norm = z != nullptr;
+    if (num_tokens < 1 || num_tokens > GDN_VERIFY_MAX_TOKENS) return GDN_ERR_SHAPE;
+    Call c{state, state_seq_stride, 4, q, k, qk_stride, v, v_stride, alpha, beta, ab_stride,
+           z, z_stride, norm_weight, eps, norm, out, 4, out_stride,
+           batch, num_tokens, num_k_heads, num_v_heads, k_dim, v_dim};
+    bool empty;
+    gdn_status s = validate(c, &empty);
+    if (s != GDN_OK || empty) return s;
+    if (num_tokens > 1) {
+        const int64_t slot = (int64_t)num_v_heads * k_dim * v_dim;
+        const int64_t slots = (int64_t)batch * (num_tokens - 1);
+        if (!inter_state) return GDN_ERR_NULL;
+        if (slots > 1 && inter_pitch < slot) return GDN_ERR_STRIDE;
+        if (!aligned(inter_state, 16) || (slots > 1 && inter_pitch % 4 != 0)) return GDN_ERR_STRIDE;
+        Span in, st, q_, k_, v_, al, be, z_, gn, o;
+        const int64_t rows = (int64_t)batch * num_tokens, vw = (int64_t)num_v_heads * v_dim;
+        const int64_t qkw = (int64_t)num_k_heads * k_dim;
+        bool ok = make_span(inter_state, slots, inter_pitch, slot, 4, &in) &&
+                  make_span(state, batch, state_seq_stride, slot, 4, &st) &&
+                  make_span(q, rows, qk_stride, qkw, 4, &q_) && make_span(k, rows, qk_stride, qkw, 4, &k_) &&
+                  make_span(v, rows, v_stride, vw, 4, &v_) &&
+                  make_span(alpha, rows, ab_stride, num_v_heads, 4, &al) &&
+                  make_span(beta, rows, ab_stride, num_v_heads, 4, &be) &&
+                  make_span(out, rows, out_stride, vw, 4, &o);
+        if (norm) ok = ok && make_span(z, rows, z_stride, vw, 4, &z_) && make_span(norm_weight, 1, v_dim, v_dim, 4, &gn);
+        if (!ok) return GDN_ERR_STRIDE;
+        const Span *others[] = {&st, &q_, &k_, &v_, &al, &be, &z_, &gn, &o};
+        for (const Span *x : others)
+            if (overlap(in, *x)) return GDN_ERR_ALIAS;
+    }
+    return finish(gdn::launch_verify(to_args(c, state, out), k_dim, inter_state, inter_pitch, norm,
+                                     (hipStream_t)stream));
+}
+
 static gdn_status check_convert(const void *src, const void *dst, int64_t n, int src_elem,
                                  int dst_elem, bool *empty) {
     *empty = false;

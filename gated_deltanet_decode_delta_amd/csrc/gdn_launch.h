@@ -37,6 +37,8 @@ enum OutMode { kOutRawF32 = 0, kOutNormF32 = 1, kOutNormBF16 = 2 };
 hipError_t launch_decode(const StepArgs &a, int dim, bool f16_state, OutMode mode,
                          hipStream_t stream);
 hipError_t launch_seq(const StepArgs &a, int dim, OutMode mode, hipStream_t stream);
+hipError_t launch_verify(const StepArgs &a, int dim, float *inter, int64_t inter_pitch, bool norm,
+                         hipStream_t stream);
 hipError_t launch_seq_mfma(const StepArgs &a, OutMode mode, hipStream_t stream);   // dim 128
 hipError_t launch_f32_to_f16(const float *src, uint16_t *dst, int64_t n, hipStream_t stream);
 hipError_t launch_f16_to_f32(const uint16_t *src, float *dst, int64_t n, hipStream_t stream);

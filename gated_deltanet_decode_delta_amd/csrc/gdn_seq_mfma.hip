@@ -278,18 +278,22 @@ __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
             }
         }
 
-        // U^T = K S^T and W^T = Q S^T on the matrix cores
-        f32x4 U = f32x4{0.f, 0.f, 0.f, 0.f}, W = U;
+        // U^T = K S^T and W^T = Q S^T on the matrix cores (four independent
+        // accumulation chains keep back-to-back MFMAs free of dependencies)
+        f32x4 Ua = f32x4{0.f, 0.f, 0.f, 0.f}, Ub = Ua, Wa = Ua, Wb = Ua;
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
             const f32x4 ka = *reinterpret_cast<const f32x4 *>(&k_s[li * kKS + 16 * m + 4 * g]);
             const f32x4 qa = *reinterpret_cast<const f32x4 *>(&q_s[li * kKS + 16 * m + 4 * g]);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                U = mfma(ka[r], S[m][r], U);
-                W = mfma(qa[r], S[m][r], W);
+            for (int r = 0; r < 4; r += 2) {
+                Ua = mfma(ka[r], S[m][r], Ua);
+                Wa = mfma(qa[r], S[m][r], Wa);
+                Ub = mfma(ka[r + 1], S[m][r + 1], Ub);
+                Wb = mfma(qa[r + 1], S[m][r + 1], Wb);
             }
         }
+        const f32x4 U = Ua + Ub, W = Wa + Wb;
         __syncthreads();   // T visible to every wave
 
         const f32x4 Ta = *reinterpret_cast<const f32x4 *>(&t_s[li * kTS + 4 * g]);
@@ -305,11 +309,20 @@ __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
             R[r] = bet[r] * (vcur[r] - pg * U[r]);
             O[r] = pg * W[r];
         }
-        Cp = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) Cp = mfma(Ta[s4], R[s4], Cp);
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) O = mfma(Ga[s4], Cp[s4], O);
+        {
+            f32x4 c0 = f32x4{0.f, 0.f, 0.f, 0.f}, c1 = c0;
+            c0 = mfma(Ta[0], R[0], c0);
+            c1 = mfma(Ta[1], R[1], c1);
+            c0 = mfma(Ta[2], R[2], c0);
+            c1 = mfma(Ta[3], R[3], c1);
+            Cp = c0 + c1;
+            f32x4 o1 = f32x4{0.f, 0.f, 0.f, 0.f};
+            O = mfma(Ga[0], Cp[0], O);
+            o1 = mfma(Ga[1], Cp[1], o1);
+            O = mfma(Ga[2], Cp[2], O);
+            o1 = mfma(Ga[3], Cp[3], o1);
+            O += o1;
+        }
         if constexpr (!NORM) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {

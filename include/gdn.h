@@ -159,6 +159,33 @@ gdn_status gdn_recurrence_seq(float *state, int64_t state_seq_stride,
                               int32_t num_v_heads, int32_t k_dim, int32_t v_dim, void *stream);
 
 /*
+ * gdn_decode_verify -- num_tokens (1..GDN_VERIFY_MAX_TOKENS) consecutive tokens
+ * per sequence in one launch, keeping the state after every token but the last
+ * for rollback: when a speculative (draft) token is rejected, the state after
+ * the last accepted token is already in inter_state.  Source: metrale
+ * ssm_gdn_a.rs, launcher `gdn_decode_chunk2` (two tokens, the intermediate
+ * state written for draft rejection), generalised to up to 8 tokens.
+ *   Token t of sequence b uses input row r = b*num_tokens + t of q, k, v, z,
+ *   alpha, beta and writes output row r (raw o when z is NULL, else y as in
+ *   gdn_decode_norm; fp32).
+ *   state        fp32 pool as in gdn_decode: read once, final state written once.
+ *   inter_state  fp32, batch*(num_tokens-1) slots of inter_pitch elements; slot
+ *                b*(num_tokens-1) + t holds the state after token t, head h at
+ *                + h*Dv*Dk (same tile layout).  May be NULL when num_tokens == 1.
+ *                Must not overlap any other buffer (GDN_ERR_ALIAS).
+ */
+#define GDN_VERIFY_MAX_TOKENS 8
+gdn_status gdn_decode_verify(float *state, int64_t state_seq_stride,
+                             float *inter_state, int64_t inter_pitch,
+                             const float *q, const float *k, int64_t qk_stride,
+                             const float *v, int64_t v_stride,
+                             const float *alpha, const float *beta, int64_t ab_stride,
+                             const float *z, int64_t z_stride, const float *norm_weight, float eps,
+                             float *out, int64_t out_stride,
+                             int32_t batch, int32_t num_tokens, int32_t num_k_heads,
+                             int32_t num_v_heads, int32_t k_dim, int32_t v_dim, void *stream);
+
+/*
  * State pool converters: n elements, fp32 -> binary16 with round to
  * nearest-even (subnormals kept, overflow to infinity, NaN stays NaN), and
  * binary16 -> fp32 (exact).  src and dst must not overlap (an in-place

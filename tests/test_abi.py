@@ -1,0 +1,180 @@
+"""The C ABI without a GPU: libgdn.so loads, exports every function that
+include/gdn.h declares, and its host-side validation returns the documented
+status codes.  Only calls that validation rejects are made here (they return
+before any HIP call), plus empty calls, which the contract makes no-ops; the
+pointers are fake addresses that are never dereferenced."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import gated_deltanet_decode_delta_amd as gdn
+    if not os.path.exists(gdn.LIB_PATH):
+        from gated_deltanet_decode_delta_amd import _build
+        _build.build()
+    return gdn.lib()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(gdn_[a-z_0-9]+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declarations_found():
+    names = _declared()
+    assert "gdn_decode" in names and "gdn_decode_verify" in names
+    assert len(names) == 9, names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    import gated_deltanet_decode_delta_amd as gdn
+    names = _declared()
+    out = subprocess.run(["nm", "-D", "--defined-only", gdn.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n), n
+    assert sorted(gdn.EXPORTS) == names       # the binding wraps exactly these
+
+
+def test_status_strings(lib):
+    for code in range(9):
+        assert lib.gdn_status_string(code)
+    assert b"unknown" in lib.gdn_status_string(99).lower()
+
+
+# fake, suitably aligned device addresses (never dereferenced)
+A = 1 << 32
+NK, NV, D, B = 2, 4, 16, 2
+SLOT = NV * D * D
+
+
+def _bases():
+    step = 1 << 24
+    names = ["state", "q", "k", "v", "alpha", "beta", "z", "gn", "out", "inter"]
+    return {n: A + i * step for i, n in enumerate(names)}
+
+
+def decode(lib, **kw):
+    p = _bases()
+    a = dict(state=p["state"], pitch=SLOT, q=p["q"], k=p["k"], qk=NK * D, v=p["v"], vs=NV * D,
+             al=p["alpha"], be=p["beta"], ab=NV, out=p["out"], os=NV * D, B=B, nk=NK, nv=NV,
+             dk=D, dv=D)
+    a.update(kw)
+    return lib.gdn_decode(a["state"], a["pitch"], a["q"], a["k"], a["qk"], a["v"], a["vs"],
+                          a["al"], a["be"], a["ab"], a["out"], a["os"], a["B"], a["nk"], a["nv"],
+                          a["dk"], a["dv"], None)
+
+
+def norm(lib, **kw):
+    p = _bases()
+    a = dict(state=p["state"], pitch=SLOT, q=p["q"], k=p["k"], qk=NK * D, v=p["v"], vs=NV * D,
+             al=p["alpha"], be=p["beta"], ab=NV, z=p["z"], zs=NV * D, gn=p["gn"], eps=1e-6,
+             out=p["out"], dt=0, os=NV * D, B=B, nk=NK, nv=NV, dk=D, dv=D)
+    a.update(kw)
+    return lib.gdn_decode_norm(a["state"], a["pitch"], a["q"], a["k"], a["qk"], a["v"], a["vs"],
+                               a["al"], a["be"], a["ab"], a["z"], a["zs"], a["gn"], a["eps"],
+                               a["out"], a["dt"], a["os"], a["B"], a["nk"], a["nv"], a["dk"],
+                               a["dv"], None)
+
+
+def seq(lib, **kw):
+    p = _bases()
+    a = dict(state=p["state"], pitch=SLOT, q=p["q"], k=p["k"], qk=NK * D, v=p["v"], vs=NV * D,
+             al=p["alpha"], be=p["beta"], ab=NV, z=None, zs=0, gn=None, eps=1e-6,
+             out=p["out"], os=NV * D, B=B, T=5, nk=NK, nv=NV, dk=D, dv=D)
+    a.update(kw)
+    return lib.gdn_recurrence_seq(a["state"], a["pitch"], a["q"], a["k"], a["qk"], a["v"],
+                                  a["vs"], a["al"], a["be"], a["ab"], a["z"], a["zs"], a["gn"],
+                                  a["eps"], a["out"], a["os"], a["B"], a["T"], a["nk"], a["nv"],
+                                  a["dk"], a["dv"], None)
+
+
+def verify(lib, **kw):
+    p = _bases()
+    a = dict(state=p["state"], pitch=SLOT, inter=p["inter"], ip=SLOT, q=p["q"], k=p["k"],
+             qk=NK * D, v=p["v"], vs=NV * D, al=p["alpha"], be=p["beta"], ab=NV, z=None, zs=0,
+             gn=None, eps=1e-6, out=p["out"], os=NV * D, B=B, T=3, nk=NK, nv=NV, dk=D, dv=D)
+    a.update(kw)
+    return lib.gdn_decode_verify(a["state"], a["pitch"], a["inter"], a["ip"], a["q"], a["k"],
+                                 a["qk"], a["v"], a["vs"], a["al"], a["be"], a["ab"], a["z"],
+                                 a["zs"], a["gn"], a["eps"], a["out"], a["os"], a["B"], a["T"],
+                                 a["nk"], a["nv"], a["dk"], a["dv"], None)
+
+
+def test_decode_validation(lib):
+    p = _bases()
+    assert decode(lib, dk=12, dv=12) == 4          # not a power of two
+    assert decode(lib, dk=512, dv=512) == 4        # above 256
+    assert decode(lib, dk=16, dv=32) == 4          # Dk != Dv
+    assert decode(lib, nv=3) == 2                  # NV % NK
+    assert decode(lib, nk=0) == 2
+    assert decode(lib, B=-1) == 2
+    assert decode(lib, q=None) == 1
+    assert decode(lib, state=None) == 1
+    assert decode(lib, pitch=SLOT - 4) == 3        # slot pitch shorter than a slot
+    assert decode(lib, qk=NK * D - 4) == 3
+    assert decode(lib, q=p["q"] + 4) == 3          # 16-byte alignment
+    assert decode(lib, qk=NK * D + 2) == 3         # row stride not a multiple of 4
+    assert decode(lib, al=p["alpha"] + 2) == 3
+    assert decode(lib, out=p["state"] + 64) == 5   # output inside the state
+    assert decode(lib, out=p["v"]) == 5            # output over an input
+    assert decode(lib, q=p["state"] + 4096) == 5   # state over an input
+    assert decode(lib, B=0) == 0                   # empty: no launch, OK
+    assert decode(lib, B=0, q=None) == 0
+
+
+def test_norm_validation(lib):
+    assert norm(lib, eps=-1.0) == 8
+    assert norm(lib, eps=float("nan")) == 8
+    assert norm(lib, eps=float("inf")) == 8
+    assert norm(lib, dt=7) == 6
+    assert norm(lib, z=None) == 1
+    assert norm(lib, gn=None) == 1
+    assert norm(lib, zs=NV * D - 4) == 3
+    p = _bases()
+    assert norm(lib, out=p["z"]) == 5
+    assert norm(lib, B=0) == 0
+
+
+def test_seq_validation(lib):
+    assert seq(lib, T=-1) == 2
+    assert seq(lib, T=0) == 0
+    assert seq(lib, vs=NV * D - 4) == 3
+    p = _bases()
+    assert seq(lib, out=p["q"]) == 5
+
+
+def test_verify_validation(lib):
+    p = _bases()
+    assert verify(lib, T=0) == 2
+    assert verify(lib, T=9) == 2
+    assert verify(lib, inter=None) == 1             # needed when T > 1
+    assert verify(lib, ip=SLOT - 4) == 3            # rollback slots overlap
+    assert verify(lib, ip=SLOT + 2) == 3            # pitch not a multiple of 4
+    assert verify(lib, inter=p["inter"] + 8) == 3   # misaligned
+    assert verify(lib, inter=p["state"]) == 5       # over the state
+    assert verify(lib, inter=p["out"] - 4 * SLOT) == 5   # tail runs into the output
+    assert verify(lib, inter=p["v"]) == 5           # over an input
+    assert verify(lib, z=p["z"], gn=None) == 1
+    assert verify(lib, B=0) == 0
+    assert verify(lib, B=0, T=9) == 2               # the token bound comes first
+
+
+def test_converter_validation(lib):
+    p = _bases()
+    assert lib.gdn_state_f32_to_f16(p["state"], p["state"] + 16, 64, None) == 5
+    assert lib.gdn_state_f32_to_f16(None, p["out"], 64, None) == 1
+    assert lib.gdn_state_f16_to_f32(p["state"], p["out"], -1, None) == 2
+    assert lib.gdn_state_f16_to_f32(p["state"], p["out"], 0, None) == 0
