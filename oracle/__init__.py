@@ -73,6 +73,16 @@ def _load():
     lib.orc_seq_head.argtypes = [i32, i32, i32, i32] + common
     lib.orc_seq.restype = i32
     lib.orc_seq.argtypes = [i32, i32, i32] + common
+    f32p = vp
+    lib.orc_frontend_token.restype = i32
+    lib.orc_frontend_token.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, dbl,
+                                       vp, vp, vp, vp, vp]
+    lib.orc_fused_decode.restype = i32
+    lib.orc_fused_decode.argtypes = [i32, i32, i32, i32, i32, f32p, i64, f32p, i64, vp, i64, vp,
+                                     vp, vp, i64, vp, vp, dbl, vp, i64, vp, dbl, vp, i64,
+                                     vp, vp, vp, vp, vp]
+    lib.orc_quant_groups32.restype = i32
+    lib.orc_quant_groups32.argtypes = [vp, i64, vp, vp]
     _lib = lib
     return lib
 
@@ -232,3 +242,81 @@ def seq_head_threaded(state, q, k, v, alpha, beta, *, B, T, NK, NV, Dk, Dv, head
     if any(rcs):
         raise RuntimeError("oracle failed")
     return out
+
+
+# --------------------------------------------------------------------------
+# front end (conv ring, silu, L2 of q and k, gates) and the fused decode
+# --------------------------------------------------------------------------
+
+def _f32(a, name):
+    if a.dtype != np.float32:
+        raise ValueError(f"{name} must be float32")
+    return a
+
+
+def frontend_token(ring: np.ndarray, x, w, br, ar, dt, rate, *, NK: int, NV: int, D: int,
+                   l2_eps: float = 1e-6):
+    """One token of one sequence through the input stage.  ``ring`` (float32,
+    C-contiguous ``[taps, C]`` with ``C = (2*NK + NV)*D``) is updated in place.
+    Returns float64 ``(q [NK*D], k [NK*D], v [NV*D], alpha [NV], beta [NV])``."""
+    taps, C = ring.shape
+    if C != (2 * NK + NV) * D or not ring.flags.c_contiguous:
+        raise ValueError("ring must be C-contiguous [taps, (2*NK+NV)*D]")
+    _f32(ring, "ring")
+    xs = np.ascontiguousarray(_f32(x, "x")).reshape(-1)
+    ws = np.ascontiguousarray(_f32(w, "w"))
+    if xs.size < C or ws.shape != (taps, C):
+        raise ValueError("x or w has the wrong shape")
+    g = [np.ascontiguousarray(_f32(a, n)).reshape(-1) for a, n in
+         ((br, "br"), (ar, "ar"), (dt, "dt"), (rate, "rate"))]
+    q = np.empty(NK * D); k = np.empty(NK * D); v = np.empty(NV * D)
+    al = np.empty(NV); be = np.empty(NV)
+    rc = _load().orc_frontend_token(NK, NV, D, taps, _ptr(ring), _ptr(xs), _ptr(ws), _ptr(g[0]),
+                                    _ptr(g[1]), _ptr(g[2]), _ptr(g[3]), float(l2_eps), _ptr(q),
+                                    _ptr(k), _ptr(v), _ptr(al), _ptr(be))
+    if rc:
+        raise RuntimeError("oracle failed")
+    return q, k, v, al, be
+
+
+def fused_decode(state: np.ndarray, ring: np.ndarray, x, w, br, ar, dt, rate, *, B: int,
+                 NK: int, NV: int, D: int, taps: int, l2_eps: float = 1e-6, z=None, gn=None,
+                 eps: float = 1e-6, return_inputs: bool = False):
+    """Front end plus one decode step for B sequences.  ``state`` (float32
+    ``[B, pitch]``) and ``ring`` (float32 ``[B, >= taps*C]``) are updated in
+    place; ``x`` is ``[B, >= C]``, ``w`` ``[taps, C]``, ``br``/``ar`` ``[B, >= NV]``,
+    ``dt``/``rate`` ``[NV]``.  Returns float64 ``[B, NV*D]`` (raw o, or y with
+    ``z``), and with ``return_inputs`` also the derived q, k, v, alpha, beta."""
+    C = (2 * NK + NV) * D
+    for a, n in ((state, "state"), (ring, "ring"), (x, "x"), (w, "w"), (br, "br"), (ar, "ar"),
+                 (dt, "dt"), (rate, "rate")):
+        _f32(a, n)
+    if ring.shape[1] < taps * C or w.shape != (taps, C) or not w.flags.c_contiguous:
+        raise ValueError("ring or w has the wrong shape")
+    if _row_stride(br) != _row_stride(ar):
+        raise ValueError("br and ar must share one row stride")
+    if z is not None:
+        _f32(z, "z"); _f32(gn, "gn")
+    out = np.empty((B, NV * D))
+    ins = [np.empty((B, NK * D)), np.empty((B, NK * D)), np.empty((B, NV * D)),
+           np.empty((B, NV)), np.empty((B, NV))] if return_inputs else [None] * 5
+    rc = _load().orc_fused_decode(B, NK, NV, D, taps, _ptr(state), state.shape[1], _ptr(ring),
+                                  _row_stride(ring), _ptr(x), _row_stride(x), _ptr(w), _ptr(br),
+                                  _ptr(ar), _row_stride(br), _ptr(np.ascontiguousarray(dt)),
+                                  _ptr(np.ascontiguousarray(rate)), float(l2_eps), _ptr(z),
+                                  _row_stride(z) if z is not None else 0, _ptr(gn), float(eps),
+                                  _ptr(out), _row_stride(out), *[_ptr(a) for a in ins])
+    if rc:
+        raise RuntimeError("oracle failed")
+    return (out, *ins) if return_inputs else out
+
+
+def quant_groups32(y) -> tuple:
+    """int8 codes and fp32 scales of a float32 vector in groups of 32 (decisions
+    in binary32).  Returns ``(codes int8 [n], scales float32 [n/32])``."""
+    ys = np.ascontiguousarray(_f32(np.asarray(y), "y")).reshape(-1)
+    codes = np.empty(ys.size, dtype=np.int8)
+    scales = np.empty(ys.size // 32, dtype=np.float32)
+    if _load().orc_quant_groups32(_ptr(ys), ys.size, _ptr(codes), _ptr(scales)):
+        raise ValueError("length must be a multiple of 32")
+    return codes, scales

@@ -25,6 +25,12 @@
  *    `gdn_prefill_regresident` and the two `ssm_h_state_*` converters: per-
  *    sequence row strides, the fp16 state pool with a slot pitch in halves,
  *    round-to-nearest-even narrowing, and the token-sequential recurrence.
+ *  - logicaffeine "codegen_cuda/gdn.rs", kernels `gk_conv_silu_l2` and
+ *    `gk_gdn_gates`, and metrale `gdn_decode_f32_conv_norm`: the input stage
+ *    fused in front of the decode (conv ring, silu, per-head L2 of q and k, the
+ *    write-strength and decay gates).
+ *  - logicaffeine "codegen_cuda/gdn.rs", kernel `gdn_gate_norm_q`: int8
+ *    quantisation of the normed output in groups of 32.
  *
  * What is computed (the plain definition, not the kernels' factoring): for value
  * head h of sequence b, with key head g = h mod NK,
@@ -273,5 +279,156 @@ int orc_seq(int B, int T, int state_kind, void *state, int64_t pitch,
                                   NK, NV, Dk, Dv);
             if (rc) return rc;
         }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Front end of the decode step: conv ring, silu, L2 of q and k, the gates.   */
+/* ------------------------------------------------------------------------- */
+
+/* One token of one sequence through the layer's input stage, in double.
+ * Source: logicaffeine codegen_cuda/gdn.rs, kernels `gk_conv_silu_l2` and
+ * `gk_gdn_gates`, and the GDN layer sequence of codegen_cuda/qwen38.rs
+ * (`emit_qwen38_generate`: the conv runs over the q|k|v channels of the
+ * projection row, the leading 2*NK head blocks are L2-normalised); metrale
+ * layers/ops/ssm_gdn_a.rs, `gdn_decode_f32_conv_norm` (the same steps fused
+ * into the decode launch, with separate L2 and norm epsilons).
+ *
+ *  channels  C = 2*NK*D + NV*D: q heads, then k heads, then v heads.
+ *  ring      taps rows of C floats, row 0 the oldest input.  The token shifts
+ *            every row up by one (row 0 is dropped) and stores x in row taps-1;
+ *            ring is updated in place (fp32 copies, exact).
+ *  conv      y_c = silu( sum_t ring'[t][c] * w[t][c] ),  w is [taps][C].
+ *  L2        each q and k head block (D channels) is divided by
+ *            sqrt(sum of its squares + l2_eps); v is not normalised.
+ *  gates     beta_h = sigmoid(br_h);  alpha_h = (1 + exp(ar_h + dt_h))^rate_h
+ *            (rate already holds the negative decay rate, so it is used as is).
+ * Outputs q, k ([NK*D]), v ([NV*D]), alpha, beta ([NV]) in double. */
+int orc_frontend_token(int NK, int NV, int D, int taps,
+                       float *ring, const float *x, const float *w,
+                       const float *br, const float *ar, const float *dt, const float *rate,
+                       double l2_eps,
+                       double *q, double *k, double *v, double *alpha, double *beta)
+{
+    if (NK <= 0 || NV <= 0 || D <= 0 || taps <= 0) return -1;
+    int64_t C = (int64_t)(2 * NK + NV) * D;
+    for (int64_t c = 0; c < C; ++c) {
+        for (int t = 0; t + 1 < taps; ++t) ring[(int64_t)t * C + c] = ring[(int64_t)(t + 1) * C + c];
+        ring[(int64_t)(taps - 1) * C + c] = x[c];
+    }
+    double *y = (double *)malloc(sizeof(double) * (size_t)C);
+    if (!y) return -1;
+    for (int64_t c = 0; c < C; ++c) {
+        double acc = 0.0;
+        for (int t = 0; t < taps; ++t)
+            acc += (double)ring[(int64_t)t * C + c] * (double)w[(int64_t)t * C + c];
+        y[c] = acc / (1.0 + exp(-acc));
+    }
+    for (int blk = 0; blk < 2 * NK; ++blk) {
+        const double *src = y + (int64_t)blk * D;
+        double ss = 0.0;
+        for (int j = 0; j < D; ++j) ss += src[j] * src[j];
+        double den = sqrt(ss + l2_eps);
+        double *dst = blk < NK ? q + (int64_t)blk * D : k + (int64_t)(blk - NK) * D;
+        for (int j = 0; j < D; ++j) dst[j] = src[j] / den;
+    }
+    for (int64_t i = 0; i < (int64_t)NV * D; ++i) v[i] = y[(int64_t)2 * NK * D + i];
+    for (int h = 0; h < NV; ++h) {
+        beta[h] = 1.0 / (1.0 + exp(-(double)br[h]));
+        alpha[h] = pow(1.0 + exp((double)ar[h] + (double)dt[h]), (double)rate[h]);
+    }
+    free(y);
+    return 0;
+}
+
+/* The fused decode: front end, then the step and the gated norm of every value
+ * head, for B sequences.  Strides are in elements: x rows x_stride apart,
+ * ring slots ring_stride apart, br/ar rows g_stride apart, z and out rows
+ * z_stride / out_stride apart.  The fp32 state is rounded once, after the step
+ * (one token).  z NULL gives the raw output o.  The q, k, v, alpha, beta that
+ * the front end produced may be returned (any of them NULL to skip), as
+ * [B][NK*D], [B][NV*D] and [B][NV]. */
+int orc_fused_decode(int B, int NK, int NV, int D, int taps,
+                     float *state, int64_t pitch,
+                     float *ring, int64_t ring_stride,
+                     const float *x, int64_t x_stride, const float *w,
+                     const float *br, const float *ar, int64_t g_stride,
+                     const float *dt, const float *rate, double l2_eps,
+                     const float *z, int64_t z_stride, const float *gn, double eps,
+                     double *out, int64_t out_stride,
+                     double *q_out, double *k_out, double *v_out, double *a_out, double *b_out)
+{
+    if (B < 0 || NK <= 0 || NV <= 0 || NV % NK || D <= 0 || taps <= 0) return -1;
+    int64_t nel = (int64_t)D * D;
+    double *q = (double *)malloc(sizeof(double) * (size_t)NK * D);
+    double *k = (double *)malloc(sizeof(double) * (size_t)NK * D);
+    double *v = (double *)malloc(sizeof(double) * (size_t)NV * D);
+    double *al = (double *)malloc(sizeof(double) * (size_t)NV);
+    double *be = (double *)malloc(sizeof(double) * (size_t)NV);
+    double *S = (double *)malloc(sizeof(double) * (size_t)nel);
+    double *o = (double *)malloc(sizeof(double) * (size_t)D);
+    double *yy = (double *)malloc(sizeof(double) * (size_t)D);
+    double *zd = (double *)malloc(sizeof(double) * (size_t)D);
+    double *gd = (double *)malloc(sizeof(double) * (size_t)D);
+    int rc = (!q || !k || !v || !al || !be || !S || !o || !yy || !zd || !gd) ? -1 : 0;
+    if (!rc && z) for (int i = 0; i < D; ++i) gd[i] = (double)gn[i];
+    for (int b = 0; b < B && !rc; ++b) {
+        rc = orc_frontend_token(NK, NV, D, taps, ring + (int64_t)b * ring_stride,
+                                x + (int64_t)b * x_stride, w, br + (int64_t)b * g_stride,
+                                ar + (int64_t)b * g_stride, dt, rate, l2_eps, q, k, v, al, be);
+        if (rc) break;
+        if (q_out) memcpy(q_out + (int64_t)b * NK * D, q, sizeof(double) * (size_t)NK * D);
+        if (k_out) memcpy(k_out + (int64_t)b * NK * D, k, sizeof(double) * (size_t)NK * D);
+        if (v_out) memcpy(v_out + (int64_t)b * NV * D, v, sizeof(double) * (size_t)NV * D);
+        if (a_out) memcpy(a_out + (int64_t)b * NV, al, sizeof(double) * (size_t)NV);
+        if (b_out) memcpy(b_out + (int64_t)b * NV, be, sizeof(double) * (size_t)NV);
+        for (int h = 0; h < NV; ++h) {
+            int g = h % NK;
+            float *slot = state + (int64_t)b * pitch + (int64_t)h * nel;
+            for (int64_t e = 0; e < nel; ++e) S[e] = (double)slot[e];
+            orc_head_step(S, q + (int64_t)g * D, k + (int64_t)g * D, v + (int64_t)h * D,
+                          al[h], be[h], D, D, o);
+            const double *res = o;
+            if (z) {
+                for (int i = 0; i < D; ++i) zd[i] = (double)z[(int64_t)b * z_stride + (int64_t)h * D + i];
+                orc_gated_rmsnorm(o, zd, gd, eps, D, yy);
+                res = yy;
+            }
+            for (int i = 0; i < D; ++i) out[(int64_t)b * out_stride + (int64_t)h * D + i] = res[i];
+            for (int64_t e = 0; e < nel; ++e) slot[e] = (float)S[e];
+        }
+    }
+    free(q); free(k); free(v); free(al); free(be); free(S); free(o); free(yy); free(zd); free(gd);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------- */
+/* int8 group quantisation of the normed output.                             */
+/* ------------------------------------------------------------------------- */
+
+/* Symmetric int8 quantisation in groups of 32 consecutive values.
+ * Source: logicaffeine codegen_cuda/gdn.rs, kernel `gdn_gate_norm_q`: per group
+ * the absolute maximum a, scale s = a / 127 (s = 1 when a == 0), and each code
+ * the value divided by s, rounded to the nearest integer with ties to even.
+ * Every decision is taken in binary32, as that kernel takes it: the input is
+ * the fp32 output vector, and a/127 and y/s are single-precision operations
+ * (this file is compiled without contraction, and x86-64 evaluates float
+ * expressions in float).  n must be a multiple of 32. */
+int orc_quant_groups32(const float *y, int64_t n, int8_t *codes, float *scales)
+{
+    if (n < 0 || n % 32) return -1;
+    for (int64_t g0 = 0; g0 < n; g0 += 32) {
+        float a = 0.0f;
+        for (int i = 0; i < 32; ++i) {
+            float m = fabsf(y[g0 + i]);
+            if (m > a) a = m;
+        }
+        float s = a > 0.0f ? a / 127.0f : 1.0f;
+        scales[g0 / 32] = s;
+        for (int i = 0; i < 32; ++i) {
+            float r = nearbyintf(y[g0 + i] / s);
+            codes[g0 + i] = (int8_t)(int)r;
+        }
+    }
     return 0;
 }

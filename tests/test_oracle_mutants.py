@@ -21,7 +21,8 @@ MUTANTS = {
     "dropped_erase_term": ("- alpha * beta * sk * k[j]", ""),
     "dropped_write_term": ("+ beta * v[i] * k[j]", ""),
     "transposed_state": ("sk += row[j] * k[j];", "sk += S[(int64_t)j * Dk + i] * k[j];"),
-    "interleaved_pairing": ("int g = h % NK;", "int g = h / (NV / NK);"),
+    "interleaved_pairing": ("int g = h % NK;                                           /* tiled",
+                            "int g = h / (NV / NK);                                    /* tiled"),
     "no_output_scale": ("double scale = 1.0 / sqrt((double)Dk);", "double scale = 1.0;"),
     "output_decayed_twice": ("acc += row[j] * q[j];", "acc += row[j] * q[j] * alpha;"),
     "eps_outside_root": ("sqrt(ss / (double)Dv + eps)", "(sqrt(ss / (double)Dv) + eps)"),
@@ -32,6 +33,22 @@ MUTANTS = {
     "no_per_step_rounding": ("if (state_kind == ORC_STATE_F32) S[e] = (double)(float)S[e];",
                              "if (state_kind == ORC_STATE_F32) S[e] = S[e];"),
     "v_row_index": ("v[r * v_stride + (int64_t)h * Dv + i]", "v[r * v_stride + (int64_t)g * Dv + i]"),
+    "conv_input_at_oldest_row": ("ring[(int64_t)(taps - 1) * C + c] = x[c];", "ring[c] = x[c];"),
+    "conv_drops_a_tap": ("for (int t = 0; t < taps; ++t)\n            acc +=",
+                         "for (int t = 1; t < taps; ++t)\n            acc +="),
+    "conv_no_silu": ("y[c] = acc / (1.0 + exp(-acc));", "y[c] = acc;"),
+    "l2_eps_outside_root": ("sqrt(ss + l2_eps)", "(sqrt(ss) + l2_eps)"),
+    "l2_over_all_of_q": ("for (int j = 0; j < D; ++j) ss += src[j] * src[j];",
+                         "for (int j = 0; j < D; ++j) ss += y[j] * y[j];"),
+    "v_takes_k_channels": ("v[i] = y[(int64_t)2 * NK * D + i]", "v[i] = y[(int64_t)NK * D + i]"),
+    "beta_sign": ("exp(-(double)br[h])", "exp((double)br[h])"),
+    "decay_sign": ("exp((double)ar[h] + (double)dt[h])", "exp(-(double)ar[h] - (double)dt[h])"),
+    "decay_without_dt": ("exp((double)ar[h] + (double)dt[h])", "exp((double)ar[h])"),
+    "fused_interleaved_pairing": ("int g = h % NK;\n            float *slot",
+                                  "int g = h / (NV / NK);\n            float *slot"),
+    "quant_scale_128": ("a / 127.0f", "a / 128.0f"),
+    "quant_truncates": ("nearbyintf(y[g0 + i] / s)", "truncf(y[g0 + i] / s)"),
+    "quant_ties_away": ("nearbyintf(y[g0 + i] / s)", "roundf(y[g0 + i] / s)"),
 }
 
 PINS = [name for name in dir(pins) if name.startswith("test_p") or name.startswith("test_f16")]

@@ -392,3 +392,194 @@ def test_f16_storage_rounds_every_step(orc):
     want = S1.astype(np.float16).view(np.uint16).reshape(1, -1)   # numpy: RNE from double
     assert np.array_equal(s16, want)
     assert np.array_equal(out[0], o)
+
+
+# ------------------------------------------------ P15: the front end ------
+def _silu(x):
+    from scipy.special import expit
+    return np.asarray(x, dtype=np.float64) * expit(np.asarray(x, dtype=np.float64))
+
+
+def _gates_zero(NV):
+    z = np.zeros(NV, dtype=np.float32)
+    return z, z.copy(), z.copy(), z.copy()
+
+
+@pytest.mark.parametrize("tap", [0, 1, 3])
+def test_p15_conv_ring_is_a_delay_line(orc, tap):
+    """A one-hot tap weight turns the depthwise causal conv into a delay line:
+    with weight 1 on tap j of a 4-deep ring, token n sees the input of token
+    n - (3 - j) (zero before the first), then silu.  The ring always holds the
+    last four inputs, oldest first.  v is neither mixed nor normalised."""
+    NK, NV, D, taps = 1, 2, 4, 4
+    C = (2 * NK + NV) * D
+    r = rng(150 + tap)
+    ring = np.zeros((taps, C), dtype=np.float32)
+    w = np.zeros((taps, C), dtype=np.float32)
+    w[tap] = 1.0
+    xs = r.standard_normal((9, C)).astype(np.float32)
+    br, ar, dt, rate = _gates_zero(NV)
+    delay = taps - 1 - tap
+    for n in range(9):
+        q, k, v, al, be = orc.frontend_token(ring, xs[n], w, br, ar, dt, rate, NK=NK, NV=NV, D=D)
+        src = xs[n - delay].astype(np.float64) if n >= delay else np.zeros(C)
+        np.testing.assert_allclose(v, _silu(src[2 * NK * D:]), rtol=1e-15, atol=1e-300)
+        hist = np.zeros((taps, C), dtype=np.float32)
+        for t in range(taps):
+            m = n - (taps - 1 - t)
+            if m >= 0:
+                hist[t] = xs[m]
+        assert np.array_equal(ring, hist), n
+        if n >= delay:   # q and k blocks point along silu of the delayed input
+            for blk, got in ((0, q), (1, k)):
+                ref = _silu(src[blk * D:(blk + 1) * D])
+                cos = got @ ref / (np.linalg.norm(got) * np.linalg.norm(ref))
+                assert cos == pytest.approx(1.0, abs=1e-14)
+
+
+def test_p15_conv_sums_every_tap(orc):
+    """All-ones weights over a ring filled with one constant c give the
+    pre-activation taps * c in every channel."""
+    NK, NV, D, taps = 1, 1, 4, 4
+    C = (2 * NK + NV) * D
+    ring = np.zeros((taps, C), dtype=np.float32)
+    w = np.ones((taps, C), dtype=np.float32)
+    br, ar, dt, rate = _gates_zero(NV)
+    c = np.float32(0.375)
+    for _ in range(taps):
+        q, k, v, _, _ = orc.frontend_token(ring, np.full(C, c, np.float32), w, br, ar, dt, rate,
+                                           NK=NK, NV=NV, D=D)
+    np.testing.assert_allclose(v, _silu(np.full(D, taps * 0.375)), rtol=1e-15)
+
+
+def test_p15_l2_normalises_q_and_k_heads(orc):
+    """Each q and each k head block is scaled to norm sqrt(s / (s + eps)), where s
+    is its squared norm before scaling (eps inside the root); with eps = 0 the
+    blocks are unit vectors.  Blocks are per head, not over all of q."""
+    NK, NV, D, taps = 3, 3, 8, 2
+    C = (2 * NK + NV) * D
+    r = rng(152)
+    w = np.zeros((taps, C), dtype=np.float32)
+    w[taps - 1] = 1.0
+    x = r.standard_normal(C).astype(np.float32)
+    x[:D] *= 10.0                            # head blocks of very different sizes
+    br, ar, dt, rate = _gates_zero(NV)
+    for eps in (0.0, 0.25):
+        ring = np.zeros((taps, C), dtype=np.float32)
+        q, k, _, _, _ = orc.frontend_token(ring, x, w, br, ar, dt, rate, NK=NK, NV=NV, D=D,
+                                           l2_eps=eps)
+        pre = _silu(x)
+        for blk in range(2 * NK):
+            s = float(pre[blk * D:(blk + 1) * D] @ pre[blk * D:(blk + 1) * D])
+            got = (q if blk < NK else k)[(blk % NK) * D:(blk % NK + 1) * D]
+            assert np.linalg.norm(got) == pytest.approx(math.sqrt(s / (s + eps)), rel=1e-14)
+
+
+def test_p15_gate_closed_forms(orc):
+    """beta = sigmoid(br): 1/2 at 0 and beta(-x) = 1 - beta(x).  The decay
+    (1 + e^(ar+dt))^rate: 1 at rate 0, 2^rate at ar + dt = 0, e^rate at
+    ar + dt = ln(e - 1), and exp(rate * softplus(ar + dt)) in general."""
+    NK, NV, D, taps = 1, 8, 4, 1
+    C = (2 * NK + NV) * D
+    r = rng(153)
+    w = np.ones((taps, C), dtype=np.float32)
+    x = np.zeros(C, dtype=np.float32)
+    br = np.array([0, 1.5, -1.5, 4, -4, 0.25, 9, -9], dtype=np.float32)
+    ar = r.uniform(-3, 3, NV).astype(np.float32)
+    dt = r.uniform(-3, 3, NV).astype(np.float32)
+    rate = -r.uniform(0.001, 0.08, NV).astype(np.float32)
+    ar[1], dt[1] = 0.0, 0.0
+    ar[2], dt[2] = np.float32(math.log(math.e - 1)), 0.0
+    rate[3] = 0.0
+    ring = np.zeros((taps, C), dtype=np.float32)
+    _, _, _, al, be = orc.frontend_token(ring, x, w, br, ar, dt, rate, NK=NK, NV=NV, D=D)
+    assert be[0] == 0.5
+    assert be[1] + be[2] == pytest.approx(1.0, abs=1e-15)
+    assert be[3] + be[4] == pytest.approx(1.0, abs=1e-15)
+    from scipy.special import expit
+    np.testing.assert_allclose(be, expit(br.astype(np.float64)), rtol=1e-15)
+    assert be[6] > 0.9998 and be[7] < 2e-4       # a large positive logit writes fully
+    assert al[3] == 1.0
+    assert al[1] == pytest.approx(2.0 ** float(rate[1]), rel=1e-15)
+    u2 = float(ar[2]) + float(dt[2])
+    assert al[2] == pytest.approx(math.exp(float(rate[2]) * math.log1p(math.exp(u2))), rel=1e-14)
+    assert al[2] == pytest.approx(math.exp(float(rate[2])), rel=1e-7)
+    u = ar.astype(np.float64) + dt.astype(np.float64)
+    np.testing.assert_allclose(al, np.exp(rate.astype(np.float64) * np.logaddexp(0.0, u)),
+                               rtol=1e-13)
+    assert ((al > 0) & (al <= 1)).all()
+
+
+def test_p15_fused_decode_composes_front_end_and_step(orc):
+    """The fused decode of a batch equals, sequence by sequence, the front end
+    followed by the pinned head step with key head g = h mod NK and the gated
+    norm; the conv ring of each sequence sits at its own (padded) stride and
+    the state pads stay untouched."""
+    B, NK, NV, D, taps = 3, 2, 6, 8, 4
+    C = (2 * NK + NV) * D
+    r = rng(154)
+    pitch = NV * D * D + 16
+    state = np.full((B, pitch), np.nan, dtype=np.float32)
+    state[:, :NV * D * D] = 0.02 * r.standard_normal((B, NV * D * D))
+    ring = np.zeros((B, taps * C + 8), dtype=np.float32)
+    ring[:, :taps * C] = r.standard_normal((B, taps * C))
+    x = r.standard_normal((B, C + 4)).astype(np.float32)
+    w = (0.5 * r.standard_normal((taps, C))).astype(np.float32)
+    gates = r.standard_normal((B, 2 * NV)).astype(np.float32)
+    br, ar = gates[:, :NV], gates[:, NV:]
+    dt = r.standard_normal(NV).astype(np.float32)
+    rate = -r.uniform(0.001, 0.08, NV).astype(np.float32)
+    z = r.standard_normal((B, NV * D)).astype(np.float32)
+    gn = (1 + 0.1 * r.standard_normal(D)).astype(np.float32)
+    st0, ring0 = state.copy(), ring.copy()
+    y = orc.fused_decode(state, ring, x, w, br, ar, dt, rate, B=B, NK=NK, NV=NV, D=D, taps=taps,
+                         z=z, gn=gn)
+    assert np.isnan(state[:, NV * D * D:]).all()
+    assert np.array_equal(ring[:, taps * C:], ring0[:, taps * C:])
+    for b in range(B):
+        rb = ring0[b, :taps * C].reshape(taps, C).copy()
+        q, k, v, al, be = orc.frontend_token(rb, x[b, :C], w, br[b], ar[b], dt, rate,
+                                             NK=NK, NV=NV, D=D)
+        assert np.array_equal(ring[b, :taps * C].reshape(taps, C), rb)
+        for h in range(NV):
+            g = h % NK
+            S = st0[b, h * D * D:(h + 1) * D * D].reshape(D, D).astype(np.float64)
+            S1, o = orc.head_step(S, q[g * D:(g + 1) * D], k[g * D:(g + 1) * D],
+                                  v[h * D:(h + 1) * D], al[h], be[h])
+            yr = orc.gated_rmsnorm(o, z[b, h * D:(h + 1) * D], gn, 1e-6)
+            np.testing.assert_allclose(y[b, h * D:(h + 1) * D], yr, rtol=1e-12, atol=1e-15)
+            assert np.array_equal(state[b, h * D * D:(h + 1) * D * D],
+                                  S1.astype(np.float32).reshape(-1))
+
+
+# ------------------------------------------- P16: int8 group quantisation --
+def test_p16_quant_exact_cases(orc):
+    """Scale = amax/127 per 32 values; ties round to even; a zero group has
+    scale 1 and zero codes; groups are 32 consecutive values."""
+    y = np.zeros(96, dtype=np.float32)
+    y[0] = 127.0                      # scale exactly 1
+    y[1:8] = [2.5, 3.5, -2.5, -3.5, 0.5, 1.5, -0.5]
+    y[32] = -12.7                     # second group: amax 12.7
+    y[33] = 6.35
+    codes, scales = orc.quant_groups32(y)
+    assert scales[0] == np.float32(1.0)
+    assert list(codes[:8]) == [127, 2, 4, -2, -4, 0, 2, 0]
+    assert scales[1] == np.float32(np.float32(12.7) / np.float32(127.0))
+    assert codes[32] == -127
+    assert scales[2] == 1.0 and not codes[64:].any()
+
+
+def test_p16_quant_round_trip_bound(orc):
+    """|y - code*scale| <= scale/2 (plus the rounding of y/scale), the group's
+    largest magnitude maps to +-127 and every code is in [-127, 127]."""
+    r = rng(160)
+    y = (r.standard_normal(32 * 64) * np.exp(r.uniform(-8, 8, 32 * 64))).astype(np.float32)
+    codes, scales = orc.quant_groups32(y)
+    ys = y.reshape(-1, 32).astype(np.float64)
+    cs = codes.reshape(-1, 32).astype(np.float64)
+    sc = scales.astype(np.float64)[:, None]
+    assert (np.abs(ys - cs * sc) <= sc * (0.5 + 1e-6)).all()
+    assert (np.abs(codes.astype(int)) <= 127).all()
+    top = np.abs(ys).argmax(axis=1)
+    assert (np.abs(cs[np.arange(cs.shape[0]), top]) == 127).all()
+    np.testing.assert_allclose(sc[:, 0], np.abs(ys).max(axis=1) / 127, rtol=1e-7)
