@@ -217,6 +217,39 @@ def run_verify(g, calls: int, pools: int = 16):
     return res
 
 
+def run_norm_q(g, calls: int, pools: int = 16):
+    """The decode workload with the int8 quantised output (codes + one scale per
+    32 values) in place of the fp32 y, rotated over state pools."""
+    import torch
+    from gated_deltanet_decode_delta_amd import inputs
+
+    c = inputs.config_case("batched")
+    B, NK, NV, D = c.B, c.NK, c.NV, c.D
+    dev = "cuda:0"
+    log(f"[bench] norm_q: B={B} pools={pools}")
+    st0 = torch.from_numpy(c.state).to(dev)
+    states = [st0.clone() for _ in range(pools)]
+    del st0
+    t = {n: torch.from_numpy(getattr(c, n)).to(dev) for n in ("q", "k", "v", "z", "alpha", "beta", "gn")}
+    codes = torch.empty((B, NV * D), dtype=torch.int8, device=dev)
+    scales = torch.empty((B, NV * D // 32), dtype=torch.float32, device=dev)
+
+    def step(i):
+        g.gdn_decode_norm_q(states[i % pools], t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["z"],
+                            t["gn"], c.eps, codes=codes, scales=scales, write_y=False,
+                            num_k_heads=NK, num_v_heads=NV)
+
+    ms = _timed(step, calls, 5)
+    algo = B * NV * (head_bytes(D, NV, NK, 4, 0, True) + D + D / 32 * 4)
+    del states, t, codes, scales
+    torch.cuda.empty_cache()
+    return {"workload": "decode + gated norm + int8 group quantisation (no fp32 y), B=64, NV=48, "
+                        "NK=16, D=128, padded pool",
+            "ms_per_call": round(ms, 5),
+            "state_GBps": round(2.0 * B * NV * D * D * 4 / ms / 1e6, 1),
+            "hbm_frac_algorithmic": round(algo / ms / 1e6 / HBM_PEAK_GBS, 4)}
+
+
 def run_real_head(g, tokens: int):
     import torch
     from gated_deltanet_decode_delta_amd import inputs
@@ -385,8 +418,9 @@ def main():
     ap.add_argument("--pools", type=int, default=48)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-extra", action="store_true", help="main workload only")
-    ap.add_argument("--extras", default="fp16_state,sequence,verify,real_head",
-                    help="comma list of extra workloads: fp16_state, sequence, verify, real_head")
+    ap.add_argument("--extras", default="fp16_state,sequence,verify,norm_q,real_head",
+                    help="comma list of extra workloads: fp16_state, sequence, verify, norm_q, "
+                         "real_head")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--seq-only", action="store_true", help="time the sequence workload alone")
     ap.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -429,7 +463,8 @@ def main():
         "note": "same pool every call: the 201 MB state can stay in the 256 MB Infinity Cache"}}
     wanted = [] if args.no_extra else [w for w in args.extras.split(",") if w]
     runners = {"fp16_state": lambda: run_fp16(g, 100), "sequence": lambda: run_seq(g, 5),
-               "verify": lambda: run_verify(g, 100), "real_head": lambda: run_real_head(g, 50)}
+               "verify": lambda: run_verify(g, 100), "norm_q": lambda: run_norm_q(g, 200),
+               "real_head": lambda: run_real_head(g, 50)}
     for w in wanted:
         extra[w] = runners[w]()
     cpu = None if args.no_cpu else cpu_baseline(args.cpu_seconds)

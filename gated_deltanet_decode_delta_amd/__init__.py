@@ -34,8 +34,8 @@ STATUS_NAMES = {
     4: "GDN_ERR_UNSUPPORTED", 5: "GDN_ERR_ALIAS", 6: "GDN_ERR_DTYPE", 7: "GDN_ERR_HIP",
     8: "GDN_ERR_ARG",
 }
-EXPORTS = ("gdn_decode", "gdn_decode_norm", "gdn_decode_f16state", "gdn_recurrence_seq",
-           "gdn_decode_verify", "gdn_state_f32_to_f16", "gdn_state_f16_to_f32",
+EXPORTS = ("gdn_decode", "gdn_decode_norm", "gdn_decode_norm_q", "gdn_decode_f16state",
+           "gdn_recurrence_seq", "gdn_decode_verify", "gdn_state_f32_to_f16", "gdn_state_f16_to_f32",
            "gdn_status_string", "gdn_last_hip_error")
 VERIFY_MAX_TOKENS = 8
 
@@ -70,12 +70,14 @@ def _lib():
     lib.gdn_decode_f16state.argtypes = norm_sig
     lib.gdn_recurrence_seq.argtypes = [vp, i64, vp, vp, i64, vp, i64, vp, vp, i64, vp, i64, vp,
                                        f32, vp, i64, i32, i32, i32, i32, i32, i32, vp]
+    lib.gdn_decode_norm_q.argtypes = [vp, i64, vp, vp, i64, vp, i64, vp, vp, i64, vp, i64, vp, f32,
+                                      vp, i64, vp, i64, vp, i64, i32, i32, i32, i32, i32, vp]
     lib.gdn_decode_verify.argtypes = [vp, i64, vp, i64, vp, vp, i64, vp, i64, vp, vp, i64, vp, i64,
                                       vp, f32, vp, i64, i32, i32, i32, i32, i32, i32, vp]
     lib.gdn_state_f32_to_f16.argtypes = [vp, vp, i64, vp]
     lib.gdn_state_f16_to_f32.argtypes = [vp, vp, i64, vp]
-    for name in ("gdn_decode", "gdn_decode_norm", "gdn_decode_f16state", "gdn_recurrence_seq",
-                 "gdn_decode_verify", "gdn_state_f32_to_f16", "gdn_state_f16_to_f32"):
+    for name in ("gdn_decode", "gdn_decode_norm", "gdn_decode_norm_q", "gdn_decode_f16state",
+                 "gdn_recurrence_seq", "gdn_decode_verify", "gdn_state_f32_to_f16", "gdn_state_f16_to_f32"):
         getattr(lib, name).restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
@@ -229,6 +231,47 @@ def gdn_decode_norm(state, q, k, v, alpha, beta, z, norm_weight, eps: float = 1e
     return _norm_call("gdn_decode_norm", state, _torch().float32, q, k, v, alpha, beta, z,
                       norm_weight, eps, out, out_dtype, num_k_heads, num_v_heads, head_dim,
                       stream, raw_ok=False)
+
+
+def gdn_decode_norm_q(state, q, k, v, alpha, beta, z, norm_weight, eps: float = 1e-6, out=None,
+                      codes=None, scales=None, *, write_y: bool = True, num_k_heads: int,
+                      num_v_heads: int, head_dim: Optional[int] = None, stream=None):
+    """One token with the fused gated RMS norm and int8 group quantisation of y.
+
+    Returns ``(y or None, codes int8 [B, NV*D], scales fp32 [B, NV*D/32])``; with
+    ``write_y=False`` (and no ``out``) y is not written at all."""
+    torch = _torch()
+    B = state.shape[0]
+    NK, NV, D = _dims(norm_weight, num_k_heads, num_v_heads, head_dim)
+    if out is None and write_y:
+        out = _empty_rows(B, NV * D, torch.float32, state)
+    if codes is None:
+        codes = _empty_rows(B, NV * D, torch.int8, state)
+    if scales is None:
+        scales = _empty_rows(B, max(NV * D // 32, 1), torch.float32, state)
+    sp, pitch = _state(state, B, NV * D * D, torch.float32)
+    qp, qs, _ = _rows(q, B, NK * D, "q", torch.float32)
+    kp, ks, _ = _rows(k, B, NK * D, "k", torch.float32)
+    if qs != ks:
+        raise ValueError("q and k must share one row stride")
+    vp_, vs, _ = _rows(v, B, NV * D, "v", torch.float32)
+    ap, abs_, _ = _rows(alpha, B, NV, "alpha", torch.float32)
+    bp, bs, _ = _rows(beta, B, NV, "beta", torch.float32)
+    if abs_ != bs:
+        raise ValueError("alpha and beta must share one row stride")
+    zp, zs, _ = _rows(z, B, NV * D, "z", torch.float32)
+    if norm_weight is None or norm_weight.dtype != torch.float32:
+        raise ValueError("norm_weight must be fp32 [D]")
+    if out is not None:
+        op, os_, _ = _rows(out, B, NV * D, "out", torch.float32)
+    else:
+        op, os_ = None, 0
+    cp, cs, _ = _rows(codes, B, NV * D, "codes", torch.int8)
+    scp, scs, _ = _rows(scales, B, NV * D // 32, "scales", torch.float32)
+    _check(_lib().gdn_decode_norm_q(sp, pitch, qp, kp, qs, vp_, vs, ap, bp, abs_, zp, zs,
+                                    norm_weight.data_ptr(), float(eps), op, os_, cp, cs, scp, scs,
+                                    B, NK, NV, D, D, _stream(state, stream)), "gdn_decode_norm_q")
+    return out, codes, scales
 
 
 def gdn_decode_f16state(state, q, k, v, alpha, beta, z=None, norm_weight=None, eps: float = 1e-6,

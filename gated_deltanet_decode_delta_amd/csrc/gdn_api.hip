@@ -62,9 +62,15 @@ struct Call {
     int out_elem;
     int64_t out_stride;
     int32_t batch, seq_len, nk, nv, dk, dv;
+    bool out_optional = false;  // out may be NULL (then it is neither checked nor written)
 };
 
-gdn_status validate(const Call &c, bool *empty) {
+// Byte ranges of every array of a validated call.
+struct Spans {
+    Span st, q, k, v, al, be, z, gn, out;
+};
+
+gdn_status validate(const Call &c, bool *empty, Spans *spans_out = nullptr) {
     *empty = false;
     if (c.batch < 0 || c.seq_len < 0) return GDN_ERR_SHAPE;
     if (c.nk <= 0 || c.nv <= 0 || c.nv % c.nk != 0) return GDN_ERR_SHAPE;
@@ -74,7 +80,9 @@ gdn_status validate(const Call &c, bool *empty) {
     if (c.norm && (!isfinite(c.eps) || c.eps < 0.0f)) return GDN_ERR_ARG;
     if (c.batch == 0 || c.seq_len == 0) { *empty = true; return GDN_OK; }
 
-    if (!c.state || !c.q || !c.k || !c.v || !c.alpha || !c.beta || !c.out) return GDN_ERR_NULL;
+    if (!c.state || !c.q || !c.k || !c.v || !c.alpha || !c.beta) return GDN_ERR_NULL;
+    if (!c.out && !c.out_optional) return GDN_ERR_NULL;
+    const bool has_out = c.out != nullptr;
     if (c.norm && (!c.z || !c.gn)) return GDN_ERR_NULL;
 
     const int64_t D = c.dk;
@@ -85,33 +93,52 @@ gdn_status validate(const Call &c, bool *empty) {
     // strides: large enough for their row (only meaningful with more than one row)
     if (c.batch > 1 && c.pitch < slot) return GDN_ERR_STRIDE;
     if (rows > 1 && (c.qk_stride < qkw || c.v_stride < vw || c.ab_stride < c.nv ||
-                     c.out_stride < vw || (c.norm && c.z_stride < vw)))
+                     (has_out && c.out_stride < vw) || (c.norm && c.z_stride < vw)))
         return GDN_ERR_STRIDE;
     // alignment of the vector-accessed arrays
     const int64_t state_vec = 16 / c.state_elem;
     if (!aligned(c.state, 16) || (c.batch > 1 && c.pitch % state_vec != 0)) return GDN_ERR_STRIDE;
     if (!aligned(c.q, 16) || !aligned(c.k, 16) || !aligned(c.v, 16) || !aligned(c.out, 16))
         return GDN_ERR_STRIDE;
-    if (rows > 1 && (c.qk_stride % 4 || c.v_stride % 4 || c.out_stride % 4)) return GDN_ERR_STRIDE;
+    if (rows > 1 && (c.qk_stride % 4 || c.v_stride % 4 || (has_out && c.out_stride % 4)))
+        return GDN_ERR_STRIDE;
     if (c.norm && (!aligned(c.z, 16) || (rows > 1 && c.z_stride % 4))) return GDN_ERR_STRIDE;
     if (!aligned(c.alpha, 4) || !aligned(c.beta, 4) || (c.norm && !aligned(c.gn, 4)))
         return GDN_ERR_STRIDE;
 
     // address ranges
-    Span st, q, k, v, al, be, z, gn, out;
+    Spans sp;
+    Span &st = sp.st, &q = sp.q, &k = sp.k, &v = sp.v, &al = sp.al, &be = sp.be, &z = sp.z,
+         &gn = sp.gn, &out = sp.out;
     bool ok = make_span(c.state, c.batch, c.pitch, slot, c.state_elem, &st) &&
               make_span(c.q, rows, c.qk_stride, qkw, 4, &q) &&
               make_span(c.k, rows, c.qk_stride, qkw, 4, &k) &&
               make_span(c.v, rows, c.v_stride, vw, 4, &v) &&
               make_span(c.alpha, rows, c.ab_stride, c.nv, 4, &al) &&
               make_span(c.beta, rows, c.ab_stride, c.nv, 4, &be) &&
-              make_span(c.out, rows, c.out_stride, vw, c.out_elem, &out);
+              make_span(c.out, has_out ? rows : 0, c.out_stride, vw, c.out_elem, &out);
     if (c.norm) ok = ok && make_span(c.z, rows, c.z_stride, vw, 4, &z) && make_span(c.gn, 1, D, D, 4, &gn);
     if (!ok) return GDN_ERR_STRIDE;
     const Span *inputs[] = {&q, &k, &v, &al, &be, &z, &gn};
     for (const Span *in : inputs)
         if (overlap(st, *in) || overlap(out, *in)) return GDN_ERR_ALIAS;
     if (overlap(st, out)) return GDN_ERR_ALIAS;
+    if (spans_out) *spans_out = sp;
+    return GDN_OK;
+}
+
+// A further output array of a validated call: `rows` rows of `width` elements,
+// `stride` apart; non-NULL, rows wide enough, base aligned to `align` bytes, and
+// overlapping no other array of the call.
+gdn_status check_extra_out(const Spans &sp, const void *p, int64_t rows, int64_t stride,
+                           int64_t width, int64_t elem, uintptr_t align, Span *span) {
+    if (!p) return GDN_ERR_NULL;
+    if (rows > 1 && stride < width) return GDN_ERR_STRIDE;
+    if (!aligned(p, align)) return GDN_ERR_STRIDE;
+    if (!make_span(p, rows, stride, width, elem, span)) return GDN_ERR_STRIDE;
+    const Span *all[] = {&sp.st, &sp.q, &sp.k, &sp.v, &sp.al, &sp.be, &sp.z, &sp.gn, &sp.out};
+    for (const Span *x : all)
+        if (overlap(*span, *x)) return GDN_ERR_ALIAS;
     return GDN_OK;
 }
 
@@ -134,6 +161,10 @@ gdn::StepArgs to_args(const Call &c, void *state, void *out) {
     a.scale = (float)(1.0 / sqrt((double)c.dk));
     a.out = out;
     a.out_stride = c.out_stride;
+    a.codes = nullptr;
+    a.codes_stride = 0;
+    a.scales = nullptr;
+    a.scales_stride = 0;
     a.batch = c.batch;
     a.seq_len = c.seq_len;
     a.nk = c.nk;
@@ -182,6 +213,39 @@ gdn_status gdn_decode_norm(float *state, int64_t state_seq_stride, const float *
     return finish(gdn::launch_decode(to_args(c, state, out), k_dim, false,
                                      out_dtype == GDN_F32 ? gdn::kOutNormF32 : gdn::kOutNormBF16,
                                      (hipStream_t)stream));
+}
+
+gdn_status gdn_decode_norm_q(float *state, int64_t state_seq_stride, const float *q,
+                             const float *k, int64_t qk_stride, const float *v, int64_t v_stride,
+                             const float *alpha, const float *beta, int64_t ab_stride,
+                             const float *z, int64_t z_stride, const float *norm_weight, float eps,
+                             float *out, int64_t out_stride, int8_t *codes, int64_t codes_stride,
+                             float *scales, int64_t scales_stride, int32_t batch,
+                             int32_t num_k_heads, int32_t num_v_heads, int32_t k_dim,
+                             int32_t v_dim, void *stream) {
+    Call c{state, state_seq_stride, 4, q, k, qk_stride, v, v_stride, alpha, beta, ab_stride,
+           z, z_stride, norm_weight, eps, true, out, 4, out_stride,
+           batch, 1, num_k_heads, num_v_heads, k_dim, v_dim};
+    c.out_optional = true;
+    bool empty;
+    Spans sp;
+    gdn_status s = validate(c, &empty, &sp);
+    if (s != GDN_OK) return s;
+    if (v_dim % 32 != 0) return GDN_ERR_UNSUPPORTED;
+    if (empty) return GDN_OK;
+    const int64_t vw = (int64_t)num_v_heads * v_dim;
+    Span cs, ss;
+    s = check_extra_out(sp, codes, batch, codes_stride, vw, 1, 1, &cs);
+    if (s != GDN_OK) return s;
+    s = check_extra_out(sp, scales, batch, scales_stride, vw / 32, 4, 4, &ss);
+    if (s != GDN_OK) return s;
+    if (overlap(cs, ss)) return GDN_ERR_ALIAS;
+    gdn::StepArgs a = to_args(c, state, out);
+    a.codes = codes;
+    a.codes_stride = codes_stride;
+    a.scales = scales;
+    a.scales_stride = scales_stride;
+    return finish(gdn::launch_decode(a, k_dim, false, gdn::kOutNormQ8, (hipStream_t)stream));
 }
 
 gdn_status gdn_decode_f16state(uint16_t *state, int64_t state_seq_stride, const float *q,
@@ -236,29 +300,16 @@ gdn_status gdn_decode_verify(float *state, int64_t state_seq_stride, float *inte
            z, z_stride, norm_weight, eps, norm, out, 4, out_stride,
            batch, num_tokens, num_k_heads, num_v_heads, k_dim, v_dim};
     bool empty;
-    gdn_status s = validate(c, &empty);
+    Spans sp;
+    gdn_status s = validate(c, &empty, &sp);
     if (s != GDN_OK || empty) return s;
     if (num_tokens > 1) {
         const int64_t slot = (int64_t)num_v_heads * k_dim * v_dim;
         const int64_t slots = (int64_t)batch * (num_tokens - 1);
-        if (!inter_state) return GDN_ERR_NULL;
-        if (slots > 1 && inter_pitch < slot) return GDN_ERR_STRIDE;
-        if (!aligned(inter_state, 16) || (slots > 1 && inter_pitch % 4 != 0)) return GDN_ERR_STRIDE;
-        Span in, st, q_, k_, v_, al, be, z_, gn, o;
-        const int64_t rows = (int64_t)batch * num_tokens, vw = (int64_t)num_v_heads * v_dim;
-        const int64_t qkw = (int64_t)num_k_heads * k_dim;
-        bool ok = make_span(inter_state, slots, inter_pitch, slot, 4, &in) &&
-                  make_span(state, batch, state_seq_stride, slot, 4, &st) &&
-                  make_span(q, rows, qk_stride, qkw, 4, &q_) && make_span(k, rows, qk_stride, qkw, 4, &k_) &&
-                  make_span(v, rows, v_stride, vw, 4, &v_) &&
-                  make_span(alpha, rows, ab_stride, num_v_heads, 4, &al) &&
-                  make_span(beta, rows, ab_stride, num_v_heads, 4, &be) &&
-                  make_span(out, rows, out_stride, vw, 4, &o);
-        if (norm) ok = ok && make_span(z, rows, z_stride, vw, 4, &z_) && make_span(norm_weight, 1, v_dim, v_dim, 4, &gn);
-        if (!ok) return GDN_ERR_STRIDE;
-        const Span *others[] = {&st, &q_, &k_, &v_, &al, &be, &z_, &gn, &o};
-        for (const Span *x : others)
-            if (overlap(in, *x)) return GDN_ERR_ALIAS;
+        Span in;
+        s = check_extra_out(sp, inter_state, slots, inter_pitch, slot, 4, 16, &in);
+        if (s != GDN_OK) return s;
+        if (slots > 1 && inter_pitch % 4 != 0) return GDN_ERR_STRIDE;
     }
     return finish(gdn::launch_verify(to_args(c, state, out), k_dim, inter_state, inter_pitch, norm,
                                      (hipStream_t)stream));

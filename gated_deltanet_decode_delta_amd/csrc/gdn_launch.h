@@ -24,15 +24,19 @@ struct StepArgs {
     const float *gn;
     float eps;
     float scale;             // 1 / sqrt(Dk)
-    void *out;
+    void *out;               // kOutNormQ8: fp32 y, may be NULL
     int64_t out_stride;
+    int8_t *codes;           // kOutNormQ8: int8 codes of y, rows codes_stride apart
+    int64_t codes_stride;
+    float *scales;           // kOutNormQ8: one scale per 32 values, rows scales_stride apart
+    int64_t scales_stride;
     int32_t batch;
     int32_t seq_len;         // 1 for decode
     int32_t nk;
     int32_t nv;
 };
 
-enum OutMode { kOutRawF32 = 0, kOutNormF32 = 1, kOutNormBF16 = 2 };
+enum OutMode { kOutRawF32 = 0, kOutNormF32 = 1, kOutNormBF16 = 2, kOutNormQ8 = 3 };
 
 hipError_t launch_decode(const StepArgs &a, int dim, bool f16_state, OutMode mode,
                          hipStream_t stream);

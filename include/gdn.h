@@ -121,6 +121,31 @@ gdn_status gdn_decode_norm(float *state, int64_t state_seq_stride,
                            int32_t k_dim, int32_t v_dim, void *stream);
 
 /*
+ * gdn_decode_norm_q -- gdn_decode_norm with the int8 activation quantisation of
+ * the output fused into the epilogue, for an int8 projection that follows.
+ * Source: logicaffeine codegen_cuda/gdn.rs, kernel `gdn_gate_norm_q`: in groups
+ * of 32 consecutive values of a head's y, scale = max|y| / 127 (1 when the group
+ * is all zero) and code = y / scale rounded to nearest, ties to even; both
+ * divisions are correctly rounded fp32 operations on the fp32 y.
+ *   out     fp32 y rows as in gdn_decode_norm, or NULL to skip writing y
+ *   codes   int8 rows of num_v_heads*v_dim, codes_stride apart (write; any alignment)
+ *   scales  fp32 rows of num_v_heads*v_dim/32, scales_stride apart (write);
+ *           scale e of row b covers codes[b][32e .. 32e+31]
+ * v_dim must be a multiple of 32 (32, 64, 128 or 256), else GDN_ERR_UNSUPPORTED.
+ * codes and scales must not overlap each other or any other array (GDN_ERR_ALIAS).
+ */
+gdn_status gdn_decode_norm_q(float *state, int64_t state_seq_stride,
+                             const float *q, const float *k, int64_t qk_stride,
+                             const float *v, int64_t v_stride,
+                             const float *alpha, const float *beta, int64_t ab_stride,
+                             const float *z, int64_t z_stride, const float *norm_weight, float eps,
+                             float *out, int64_t out_stride,
+                             int8_t *codes, int64_t codes_stride,
+                             float *scales, int64_t scales_stride,
+                             int32_t batch, int32_t num_k_heads, int32_t num_v_heads,
+                             int32_t k_dim, int32_t v_dim, void *stream);
+
+/*
  * gdn_decode_f16state -- the IEEE binary16 state twin of gdn_decode_norm.
  * The state is read as binary16, all arithmetic is fp32, and the updated state
  * is rounded to nearest-even binary16 on store (subnormals kept).

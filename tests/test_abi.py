@@ -33,7 +33,7 @@ def _declared():
 def test_header_declarations_found():
     names = _declared()
     assert "gdn_decode" in names and "gdn_decode_verify" in names
-    assert len(names) == 9, names
+    assert len(names) == 10, names
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -170,6 +170,37 @@ def test_verify_validation(lib):
     assert verify(lib, z=p["z"], gn=None) == 1
     assert verify(lib, B=0) == 0
     assert verify(lib, B=0, T=9) == 2               # the token bound comes first
+
+
+def normq(lib, **kw):
+    p = _bases()
+    a = dict(state=p["state"], pitch=SLOT, q=p["q"], k=p["k"], qk=NK * D, v=p["v"], vs=NV * D,
+             al=p["alpha"], be=p["beta"], ab=NV, z=p["z"], zs=NV * D, gn=p["gn"], eps=1e-6,
+             out=p["out"], os=NV * D, codes=p["inter"], cs=NV * D, scales=p["inter"] + (1 << 20),
+             ss=NV * D // 32, B=B, nk=NK, nv=NV, dk=D, dv=D)
+    a.update(kw)
+    return lib.gdn_decode_norm_q(a["state"], a["pitch"], a["q"], a["k"], a["qk"], a["v"], a["vs"],
+                                 a["al"], a["be"], a["ab"], a["z"], a["zs"], a["gn"], a["eps"],
+                                 a["out"], a["os"], a["codes"], a["cs"], a["scales"], a["ss"],
+                                 a["B"], a["nk"], a["nv"], a["dk"], a["dv"], None)
+
+
+def test_norm_q_validation(lib):
+    p = _bases()
+    assert normq(lib) == 4                               # D = 16: not a multiple of 32
+    big = dict(dk=32, dv=32, pitch=NV * 32 * 32, vs=NV * 32, zs=NV * 32, os=NV * 32,
+               cs=NV * 32, ss=NV, qk=NK * 32)
+    assert normq(lib, codes=None, **big) == 1
+    assert normq(lib, scales=None, **big) == 1
+    assert normq(lib, **dict(big, cs=NV * 32 - 1)) == 3  # codes rows too short
+    assert normq(lib, **dict(big, ss=NV - 1)) == 3
+    assert normq(lib, scales=p["inter"] + (1 << 20) + 2, **big) == 3   # scales misaligned
+    assert normq(lib, scales=p["inter"] + 64, **big) == 5              # scales inside codes
+    assert normq(lib, codes=p["state"] + 16, **big) == 5               # codes over the state
+    assert normq(lib, codes=p["out"], **big) == 5                      # codes over y
+    assert normq(lib, scales=p["q"], **big) == 5                       # scales over an input
+    assert normq(lib, out=None, z=None, **big) == 1                    # z is required
+    assert normq(lib, B=0, **big) == 0
 
 
 def test_converter_validation(lib):
