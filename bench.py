@@ -250,6 +250,53 @@ def run_norm_q(g, calls: int, pools: int = 16):
             "hbm_frac_algorithmic": round(algo / ms / 1e6 / HBM_PEAK_GBS, 4)}
 
 
+def run_fused(g, calls: int, pools: int = 16):
+    """The decode workload with the input stage fused in front (4-tap conv ring,
+    silu, L2 of q/k, gates): one launch per layer from the projection row, with
+    the ring updated in place and with two alternating ring buffers."""
+    import torch
+    from gated_deltanet_decode_delta_amd import inputs
+
+    B, NK, NV, D, taps = 64, 16, 48, 128, 4
+    c = inputs.make_frontend_case(3200, B=B, NK=NK, NV=NV, D=D, taps=taps, pitch=983040)
+    dev = "cuda:0"
+    st0 = torch.from_numpy(c.state).to(dev)
+    states = [st0.clone() for _ in range(pools)]
+    del st0
+    r0 = torch.from_numpy(c.ring).to(dev)
+    rings = [[r0.clone(), r0.clone()] for _ in range(pools)]
+    del r0
+    t = {n: torch.from_numpy(getattr(c, n)).to(dev) for n in ("x", "w", "br", "ar", "dt", "rate", "z", "gn")}
+    out = torch.empty((B, NV * D), device=dev)
+    C = c.C
+    algo = (2.0 * B * NV * D * D * 4                      # state read + write
+            + B * (2 * taps - 1) * C * 4.0                # ring: taps-1 rows read, taps rows written
+            + B * C * 4.0 + taps * C * 4.0                # x, conv weights
+            + B * NV * (2 * 4 + 2 * D * 4) + NV * 8.0)    # br, ar, z, y; dt, rate
+    res = {"workload": "decode with fused input stage (4-tap conv ring, silu, L2 q/k, gates) and "
+                       "gated norm, B=64, NV=48, NK=16, D=128, padded pool",
+           "algorithmic_bytes_per_launch": int(algo)}
+    for mode in ("in_place", "two_buffers"):
+        log(f"[bench] fused input stage ({mode}): B={B} pools={pools}")
+
+        def step(i):
+            p = i % pools
+            pair = rings[p]
+            src, dst = (pair[0], None) if mode == "in_place" else (pair[(i // pools) % 2],
+                                                                    pair[(i // pools + 1) % 2])
+            g.gdn_decode_fused(states[p], src, t["x"], t["w"], t["br"], t["ar"], t["dt"], t["rate"],
+                               t["z"], t["gn"], 1e-6, 1e-6, out=out, conv_state_out=dst,
+                               num_k_heads=NK, num_v_heads=NV)
+
+        ms = _timed(step, calls, 5)
+        res[mode] = {"ms_per_call": round(ms, 5),
+                     "state_GBps": round(2.0 * B * NV * D * D * 4 / ms / 1e6, 1),
+                     "hbm_frac_algorithmic": round(algo / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    del states, rings, t, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_real_head(g, tokens: int):
     import torch
     from gated_deltanet_decode_delta_amd import inputs
@@ -418,9 +465,9 @@ def main():
     ap.add_argument("--pools", type=int, default=48)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-extra", action="store_true", help="main workload only")
-    ap.add_argument("--extras", default="fp16_state,sequence,verify,norm_q,real_head",
+    ap.add_argument("--extras", default="fp16_state,sequence,verify,norm_q,fused,real_head",
                     help="comma list of extra workloads: fp16_state, sequence, verify, norm_q, "
-                         "real_head")
+                         "fused, real_head")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--seq-only", action="store_true", help="time the sequence workload alone")
     ap.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -464,6 +511,7 @@ def main():
     wanted = [] if args.no_extra else [w for w in args.extras.split(",") if w]
     runners = {"fp16_state": lambda: run_fp16(g, 100), "sequence": lambda: run_seq(g, 5),
                "verify": lambda: run_verify(g, 100), "norm_q": lambda: run_norm_q(g, 200),
+               "fused": lambda: run_fused(g, 200),
                "real_head": lambda: run_real_head(g, 50)}
     for w in wanted:
         extra[w] = runners[w]()

@@ -35,8 +35,8 @@ STATUS_NAMES = {
     8: "GDN_ERR_ARG",
 }
 EXPORTS = ("gdn_decode", "gdn_decode_norm", "gdn_decode_norm_q", "gdn_decode_f16state",
-           "gdn_recurrence_seq", "gdn_decode_verify", "gdn_state_f32_to_f16", "gdn_state_f16_to_f32",
-           "gdn_status_string", "gdn_last_hip_error")
+           "gdn_recurrence_seq", "gdn_decode_verify", "gdn_decode_fused", "gdn_state_f32_to_f16",
+           "gdn_state_f16_to_f32", "gdn_status_string", "gdn_last_hip_error")
 VERIFY_MAX_TOKENS = 8
 
 
@@ -72,12 +72,14 @@ def _lib():
                                        f32, vp, i64, i32, i32, i32, i32, i32, i32, vp]
     lib.gdn_decode_norm_q.argtypes = [vp, i64, vp, vp, i64, vp, i64, vp, vp, i64, vp, i64, vp, f32,
                                       vp, i64, vp, i64, vp, i64, i32, i32, i32, i32, i32, vp]
+    lib.gdn_decode_fused.argtypes = [vp, i64, vp, i64, vp, vp, i64, vp, i32, vp, vp, i64, vp, vp, f32,
+                                     vp, i64, vp, f32, vp, i64, i32, i32, i32, i32, i32, vp]
     lib.gdn_decode_verify.argtypes = [vp, i64, vp, i64, vp, vp, i64, vp, i64, vp, vp, i64, vp, i64,
                                       vp, f32, vp, i64, i32, i32, i32, i32, i32, i32, vp]
     lib.gdn_state_f32_to_f16.argtypes = [vp, vp, i64, vp]
     lib.gdn_state_f16_to_f32.argtypes = [vp, vp, i64, vp]
     for name in ("gdn_decode", "gdn_decode_norm", "gdn_decode_norm_q", "gdn_decode_f16state",
-                 "gdn_recurrence_seq", "gdn_decode_verify", "gdn_state_f32_to_f16", "gdn_state_f16_to_f32"):
+                 "gdn_recurrence_seq", "gdn_decode_verify", "gdn_decode_fused", "gdn_state_f32_to_f16", "gdn_state_f16_to_f32"):
         getattr(lib, name).restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
@@ -360,6 +362,60 @@ def gdn_decode_verify(state, q, k, v, alpha, beta, z=None, norm_weight=None, eps
                                     gp, float(eps), op, os_, B, T, NK, NV, D, D,
                                     _stream(state, stream)), "gdn_decode_verify")
     return out, inter_state
+
+
+def gdn_decode_fused(state, conv_state, x, conv_weight, br, ar, dt_bias, decay_rate, z=None,
+                     norm_weight=None, eps: float = 1e-6, l2_eps: float = 1e-6, out=None,
+                     conv_state_out=None, *, num_k_heads: int, num_v_heads: int,
+                     head_dim: Optional[int] = None, stream=None):
+    """One token with the input stage fused in front of the step.
+
+    ``x`` holds the projection rows ``[B, >= C]`` (channels q | k | v, before the
+    conv), ``conv_state`` the rings ``[B, taps*C]`` (or ``[B, taps, C]``, updated),
+    ``conv_weight`` ``[taps, C]``, ``br``/``ar`` ``[B, >= NV]`` and
+    ``dt_bias``/``decay_rate`` ``[NV]``.  With ``conv_state_out`` (same shape and
+    row stride as ``conv_state``) the new ring goes there and ``conv_state`` is
+    only read.  Returns o, or y when ``z`` is given."""
+    torch = _torch()
+    B = state.shape[0]
+    NK, NV, D = _dims(norm_weight, num_k_heads, num_v_heads, head_dim)
+    C = (2 * NK + NV) * D
+    if conv_weight.dim() != 2 or conv_weight.shape[1] != C or not conv_weight.is_contiguous():
+        raise ValueError(f"conv_weight must be contiguous [taps, {C}]")
+    taps = conv_weight.shape[0]
+    if out is None:
+        out = _empty_rows(B, NV * D, torch.float32, state)
+    sp, pitch = _state(state, B, NV * D * D, torch.float32)
+    rp, rpitch = _state(conv_state, B, taps * C, torch.float32)
+    if conv_state_out is not None:
+        rop, ropitch = _state(conv_state_out, B, taps * C, torch.float32)
+        if B > 1 and ropitch != rpitch:
+            raise ValueError("conv_state_out must have conv_state's row stride")
+    else:
+        rop = None
+    xp, xs, _ = _rows(x, B, C, "x", torch.float32)
+    bp, bs, _ = _rows(br, B, NV, "br", torch.float32)
+    ap, as_, _ = _rows(ar, B, NV, "ar", torch.float32)
+    if bs != as_:
+        raise ValueError("br and ar must share one row stride")
+    for t, n in ((dt_bias, "dt_bias"), (decay_rate, "decay_rate"), (conv_weight, "conv_weight")):
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous fp32 device tensor")
+    if dt_bias.numel() != NV or decay_rate.numel() != NV:
+        raise ValueError("dt_bias and decay_rate must hold num_v_heads values")
+    if z is not None:
+        zp, zs, _ = _rows(z, B, NV * D, "z", torch.float32)
+        if norm_weight is None or norm_weight.dtype != torch.float32:
+            raise ValueError("norm_weight must be fp32 [D]")
+        gp = norm_weight.data_ptr()
+    else:
+        zp, zs, gp = None, 0, None
+    op, os_, _ = _rows(out, B, NV * D, "out", torch.float32)
+    _check(_lib().gdn_decode_fused(sp, pitch, rp, rpitch, rop, xp, xs, conv_weight.data_ptr(), taps, bp,
+                                   ap, bs, dt_bias.data_ptr(), decay_rate.data_ptr(), float(l2_eps),
+                                   zp, zs, gp, float(eps), op, os_, B, NK, NV, D, D,
+                                   _stream(state, stream)), "gdn_decode_fused")
+    return out
 
 
 def gdn_state_f32_to_f16(src, dst=None, stream=None):

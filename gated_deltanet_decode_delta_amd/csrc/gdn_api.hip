@@ -315,6 +315,100 @@ gdn_status gdn_decode_verify(float *state, int64_t state_seq_stride, float *inte
                                      (hipStream_t)stream));
 }
 
+gdn_status gdn_decode_fused(float *state, int64_t state_seq_stride, float *conv_state,
+                            int64_t conv_seq_stride, float *conv_state_out, const float *x,
+                            int64_t x_stride,
+                            const float *conv_weight, int32_t taps, const float *br,
+                            const float *ar, int64_t gate_stride, const float *dt_bias,
+                            const float *decay_rate, float l2_eps, const float *z,
+                            int64_t z_stride, const float *norm_weight, float eps, float *out,
+                            int64_t out_stride, int32_t batch, int32_t num_k_heads,
+                            int32_t num_v_heads, int32_t k_dim, int32_t v_dim, void *stream) {
+    const bool norm = z != nullptr;
+    if (batch < 0 || num_k_heads <= 0 || num_v_heads <= 0 || num_v_heads % num_k_heads != 0 ||
+        k_dim <= 0 || v_dim <= 0 || taps < 1 || taps > gdn::kMaxTaps)
+        return GDN_ERR_SHAPE;
+    if (k_dim != v_dim || !supported_dim(k_dim)) return GDN_ERR_UNSUPPORTED;
+    if ((int64_t)batch * num_k_heads > INT32_MAX) return GDN_ERR_SHAPE;
+    if (!isfinite(l2_eps) || l2_eps < 0.0f) return GDN_ERR_ARG;
+    if (norm && (!isfinite(eps) || eps < 0.0f)) return GDN_ERR_ARG;
+    const int32_t D = k_dim;
+    const bool in_place = conv_state_out == nullptr;
+    if (in_place && gdn::fused_lds_bytes(D, num_v_heads / num_k_heads) > 64 * 1024)
+        return GDN_ERR_UNSUPPORTED;
+    if (batch == 0) return GDN_OK;
+
+    if (!state || !conv_state || !x || !conv_weight || !br || !ar || !dt_bias || !decay_rate || !out)
+        return GDN_ERR_NULL;
+    if (norm && !norm_weight) return GDN_ERR_NULL;
+    const int64_t slot = (int64_t)num_v_heads * D * D;
+    const int64_t ch = (int64_t)(2 * num_k_heads + num_v_heads) * D;
+    const int64_t ring = taps * ch;
+    const int64_t vw = (int64_t)num_v_heads * D;
+    const bool many = batch > 1;
+    if (many && (state_seq_stride < slot || conv_seq_stride < ring || x_stride < ch ||
+                 gate_stride < num_v_heads || out_stride < vw || (norm && z_stride < vw)))
+        return GDN_ERR_STRIDE;
+    if (!aligned(state, 16) || !aligned(conv_state, 16) || !aligned(conv_state_out, 16) ||
+        !aligned(x, 16) ||
+        !aligned(conv_weight, 16) || !aligned(out, 16) || (norm && !aligned(z, 16)))
+        return GDN_ERR_STRIDE;
+    if (many && (state_seq_stride % 4 || conv_seq_stride % 4 || x_stride % 4 || out_stride % 4 ||
+                 (norm && z_stride % 4)))
+        return GDN_ERR_STRIDE;
+    if (!aligned(br, 4) || !aligned(ar, 4) || !aligned(dt_bias, 4) || !aligned(decay_rate, 4) ||
+        (norm && !aligned(norm_weight, 4)))
+        return GDN_ERR_STRIDE;
+
+    Span st, rg, ro, xs, w, b_, a_, dt, rt, z_, gn, o;
+    bool ok = make_span(state, batch, state_seq_stride, slot, 4, &st) &&
+              make_span(conv_state_out, in_place ? 0 : batch, conv_seq_stride, ring, 4, &ro) &&
+              make_span(conv_state, batch, conv_seq_stride, ring, 4, &rg) &&
+              make_span(x, batch, x_stride, ch, 4, &xs) &&
+              make_span(conv_weight, 1, ring, ring, 4, &w) &&
+              make_span(br, batch, gate_stride, num_v_heads, 4, &b_) &&
+              make_span(ar, batch, gate_stride, num_v_heads, 4, &a_) &&
+              make_span(dt_bias, 1, num_v_heads, num_v_heads, 4, &dt) &&
+              make_span(decay_rate, 1, num_v_heads, num_v_heads, 4, &rt) &&
+              make_span(out, batch, out_stride, vw, 4, &o);
+    if (norm) ok = ok && make_span(z, batch, z_stride, vw, 4, &z_) && make_span(norm_weight, 1, D, D, 4, &gn);
+    if (!ok) return GDN_ERR_STRIDE;
+    const Span *written[] = {&st, &rg, &ro, &o};   // rg is only read when ro is given
+    const Span *all[] = {&st, &rg, &ro, &o, &xs, &w, &b_, &a_, &dt, &rt, &z_, &gn};
+    for (const Span *wr : written)
+        for (const Span *x2 : all)
+            if (wr != x2 && overlap(*wr, *x2)) return GDN_ERR_ALIAS;
+
+    gdn::StepArgs a{};
+    a.state = state;
+    a.pitch = state_seq_stride;
+    a.z = z;
+    a.z_stride = z_stride;
+    a.gn = norm_weight;
+    a.eps = eps;
+    a.scale = (float)(1.0 / sqrt((double)D));
+    a.out = out;
+    a.out_stride = out_stride;
+    a.batch = batch;
+    a.seq_len = 1;
+    a.nk = num_k_heads;
+    a.nv = num_v_heads;
+    gdn::FrontArgs f;
+    f.ring = conv_state;
+    f.ring_stride = conv_seq_stride;
+    f.x = x;
+    f.x_stride = x_stride;
+    f.w = conv_weight;
+    f.taps = taps;
+    f.br = br;
+    f.ar = ar;
+    f.g_stride = gate_stride;
+    f.dt = dt_bias;
+    f.rate = decay_rate;
+    f.l2_eps = l2_eps;
+    return finish(gdn::launch_fused(a, f, conv_state_out, D, norm, (hipStream_t)stream));
+}
+
 static gdn_status check_convert(const void *src, const void *dst, int64_t n, int src_elem,
                                  int dst_elem, bool *empty) {
     *empty = false;

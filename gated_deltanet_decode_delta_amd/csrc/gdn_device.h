@@ -56,14 +56,14 @@ __device__ __forceinline__ float group_sum_wide(float x) {
     }
 }
 
-// fp32 -> bfloat16 bits, round to nearest even; NaN stays a quiet NaN.
-// maximum over each aligned group of 32 lanes of a wave64
+// Maximum over each aligned group of 32 lanes of a wave64 (ds_bpermute).
 __device__ __forceinline__ float group_max32(float x) {
 #pragma unroll
     for (int off = 16; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 32));
     return x;
 }
 
+// fp32 -> bfloat16 bits, round to nearest even; NaN stays a quiet NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     uint32_t u = __float_as_uint(f);
     if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);

@@ -36,6 +36,25 @@ struct StepArgs {
     int32_t nv;
 };
 
+// The layer's input stage fused in front of the decode: conv ring, weights,
+// raw gate inputs and per-head gate parameters (strides in elements).
+struct FrontArgs {
+    float *ring;             // [B] slots of taps rows of C = (2 NK + NV) D channels
+    int64_t ring_stride;
+    const float *x;          // this token's projection rows, channels q | k | v
+    int64_t x_stride;
+    const float *w;          // [taps][C]
+    int32_t taps;
+    const float *br;         // write-strength logits, rows g_stride apart
+    const float *ar;         // decay inputs, same rows
+    int64_t g_stride;
+    const float *dt;         // [NV] decay bias
+    const float *rate;       // [NV] decay exponent (negative)
+    float l2_eps;
+};
+
+constexpr int kMaxTaps = 8;
+
 enum OutMode { kOutRawF32 = 0, kOutNormF32 = 1, kOutNormBF16 = 2, kOutNormQ8 = 3 };
 
 hipError_t launch_decode(const StepArgs &a, int dim, bool f16_state, OutMode mode,
@@ -43,6 +62,11 @@ hipError_t launch_decode(const StepArgs &a, int dim, bool f16_state, OutMode mod
 hipError_t launch_seq(const StepArgs &a, int dim, OutMode mode, hipStream_t stream);
 hipError_t launch_verify(const StepArgs &a, int dim, float *inter, int64_t inter_pitch, bool norm,
                          hipStream_t stream);
+// ring_out NULL: the ring is updated in place (one workgroup per key head);
+// otherwise the new ring goes to ring_out (one workgroup per value head)
+hipError_t launch_fused(const StepArgs &a, const FrontArgs &f, float *ring_out, int dim, bool norm,
+                        hipStream_t stream);
+size_t fused_lds_bytes(int dim, int heads_per_key_head);
 hipError_t launch_seq_mfma(const StepArgs &a, OutMode mode, hipStream_t stream);   // dim 128
 hipError_t launch_f32_to_f16(const float *src, uint16_t *dst, int64_t n, hipStream_t stream);
 hipError_t launch_f16_to_f32(const uint16_t *src, float *dst, int64_t n, hipStream_t stream);

@@ -1,0 +1,42 @@
+// gdn_tile.h -- the register mapping of one value head's D x D state tile used
+// by the decode-shaped kernels (single-token decode, draft verify, and the
+// decode with the fused input stage).  Each kernel writes its token loop out in
+// full over this mapping: the register allocator keeps the tile in VGPRs only
+// when the loads, the update and the stores sit in one straight-line body.
+//
+// A row of the tile is covered by LPR consecutive lanes (16 at D = 128, one DPP
+// row) that each hold NCH 16-byte vectors of it, interleaved so that one load
+// instruction of 16 lanes covers 256 contiguous bytes; a lane keeps RPL rows.
+// At D = 128 (fp32) a 256-thread workgroup holds the whole 64 KiB tile as 16
+// float4 per lane.  The per-row sums S_i.k and S_i.q are in-row DPP
+// all-reductions, so every lane of a row ends with u_i, w_i, coef_i and o_i and
+// updates its own columns directly.
+#pragma once
+
+#include "gdn_device.h"
+
+namespace gdn {
+
+template <typename T, int N>
+struct VecT {
+    typedef T type __attribute__((ext_vector_type(N)));
+};
+
+template <int D, typename ST>
+struct DecodeTile {
+    static constexpr int kMaxVec = 16 / (int)sizeof(ST);
+    static constexpr int VEC = kMaxVec < D ? kMaxVec : D;     // state elements per vector access
+    static constexpr int LPR = (D / VEC) < 16 ? D / VEC : 16; // lanes per row
+    static constexpr int NCH = D / (LPR * VEC);               // vectors per lane per row
+    static constexpr int C = NCH * VEC;                       // columns per lane
+    static constexpr int NT_RAW = D * D / 64;                 // aim: 64 state values per lane
+    static constexpr int NT = NT_RAW < 64 ? 64 : (NT_RAW > 1024 ? 1024 : NT_RAW);
+    static constexpr int NG = NT / LPR;                       // row groups
+    static constexpr int RPL = (D / NG) < 1 ? 1 : D / NG;     // rows per lane
+    static constexpr int NGA = D / RPL;                       // row groups holding rows
+    static_assert(VEC % 4 == 0, "q/k are read as float4");
+    static_assert(RPL <= LPR, "one output row per lane");
+    static_assert(NGA <= NG, "rows fit the workgroup");
+};
+
+}  // namespace gdn

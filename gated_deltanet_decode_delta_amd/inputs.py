@@ -96,3 +96,59 @@ def config_case(name: str, **overrides) -> Case:
         cfg.pop(extra, None)
     seed = cfg.pop("seed")
     return make_case(seed, **cfg)
+
+
+@dataclass
+class FrontCase:
+    """Inputs of the decode with the fused input stage (conv ring, L2, gates)."""
+    B: int
+    NK: int
+    NV: int
+    D: int
+    taps: int
+    pitch: int
+    state: np.ndarray          # float32 [B, pitch]; pads hold NaN
+    ring: np.ndarray           # float32 [B, ring_pitch]: taps rows of C channels, pads NaN
+    x: np.ndarray              # float32 [B, C]: projection rows, channels q | k | v
+    w: np.ndarray              # float32 [taps, C]
+    br: np.ndarray             # float32 [B, NV]
+    ar: np.ndarray             # float32 [B, NV]
+    dt: np.ndarray             # float32 [NV]
+    rate: np.ndarray           # float32 [NV], negative
+    z: np.ndarray              # float32 [B, NV*D]
+    gn: np.ndarray             # float32 [D]
+    eps: float = 1e-6
+    l2_eps: float = 1e-6
+
+    @property
+    def C(self) -> int:
+        return (2 * self.NK + self.NV) * self.D
+
+
+def make_frontend_case(seed: int, *, B: int, NK: int, NV: int, D: int, taps: int = 4,
+                       pitch: Optional[int] = None, ring_pitch: Optional[int] = None) -> FrontCase:
+    """Draw one fused-input-stage workload from one PCG64 stream, in this order:
+    gn = 1 + 0.1 N; state 0.02 N; ring N(0,1) (earlier projection rows); x N(0,1);
+    conv weights 0.5 N; br, ar N(0,1); dt 0.5 N; rate = -U(0.001, 0.08) (all
+    negative and small, the decay exponents the model stores); z N(0,1)."""
+    C = (2 * NK + NV) * D
+    dense = NV * D * D
+    pitch = dense if pitch is None else int(pitch)
+    ring_pitch = taps * C if ring_pitch is None else int(ring_pitch)
+    if pitch < dense or ring_pitch < taps * C:
+        raise ValueError("pitch smaller than a slot")
+    rng = np.random.Generator(np.random.PCG64(seed))
+    gn = (1.0 + 0.1 * rng.standard_normal(D)).astype(np.float32)
+    state = np.full((B, pitch), np.nan, dtype=np.float32)
+    state[:, :dense] = 0.02 * rng.standard_normal((B, dense), dtype=np.float32)
+    ring = np.full((B, ring_pitch), np.nan, dtype=np.float32)
+    ring[:, :taps * C] = rng.standard_normal((B, taps * C), dtype=np.float32)
+    x = rng.standard_normal((B, C), dtype=np.float32)
+    w = (0.5 * rng.standard_normal((taps, C))).astype(np.float32)
+    br = rng.standard_normal((B, NV), dtype=np.float32)
+    ar = rng.standard_normal((B, NV), dtype=np.float32)
+    dt = (0.5 * rng.standard_normal(NV)).astype(np.float32)
+    rate = (-rng.uniform(0.001, 0.08, NV)).astype(np.float32)
+    z = rng.standard_normal((B, NV * D), dtype=np.float32)
+    return FrontCase(B=B, NK=NK, NV=NV, D=D, taps=taps, pitch=pitch, state=state, ring=ring, x=x,
+                     w=w, br=br, ar=ar, dt=dt, rate=rate, z=z, gn=gn)

@@ -211,6 +211,51 @@ gdn_status gdn_decode_verify(float *state, int64_t state_seq_stride,
                              int32_t num_v_heads, int32_t k_dim, int32_t v_dim, void *stream);
 
 /*
+ * gdn_decode_fused -- one token with the layer's input stage fused in front of
+ * the step: the projection row x (channels q | k | v, before the conv) goes
+ * through the depthwise causal conv over the sequence's ring of the last `taps`
+ * rows and silu; every q and k head block is divided by sqrt(sum of its squares
+ * + l2_eps); beta = sigmoid(br) and alpha = (1 + exp(ar + dt_bias))^decay_rate
+ * per value head; then the step (and, with z, the gated RMS norm) of
+ * gdn_decode / gdn_decode_norm.  Sources: logicaffeine codegen_cuda/gdn.rs,
+ * kernels `gk_conv_silu_l2` and `gk_gdn_gates`; metrale ssm_gdn_a.rs, launcher
+ * `gdn_decode_f32_conv_norm`.
+ *   C = (2*num_k_heads + num_v_heads) * D channels (D = k_dim = v_dim).
+ *   conv_state   fp32, per sequence taps rows of C channels, row 0 the oldest;
+ *                slot b at conv_state + b*conv_seq_stride, row t at + t*C.
+ *                The new ring is the old one shifted up by one row with x
+ *                appended as row taps-1.
+ *   conv_state_out  NULL: the new ring replaces the old one in place (one
+ *                workgroup per key head owns its channels; the features of
+ *                its NV/NK value heads must fit 64 KiB of LDS, else
+ *                GDN_ERR_UNSUPPORTED).  Otherwise a second buffer of the same
+ *                layout and stride that receives the new ring while conv_state
+ *                is only read (one workgroup per value head; faster); callers
+ *                alternate the two buffers from token to token.
+ *   x            fp32 rows of >= C, x_stride apart (read)
+ *   conv_weight  fp32 [taps][C] (read); taps in [1, 8]
+ *   br, ar       fp32 rows of >= num_v_heads, gate_stride apart (read)
+ *   dt_bias, decay_rate  fp32 [num_v_heads] (read); decay_rate is the negative
+ *                exponent itself (no further exp is applied)
+ *   l2_eps       >= 0, inside the square root of the q/k normalisation
+ *   z            NULL: raw o is written; else the gated norm as gdn_decode_norm
+ *   out          fp32 rows of num_v_heads*v_dim, out_stride apart (write)
+ * state, conv_state, conv_state_out and out must not overlap each other or any
+ * input (GDN_ERR_ALIAS).  conv_state(_out), x and conv_weight need 16-byte
+ * alignment and (for batch > 1) strides that are multiples of 4.
+ */
+gdn_status gdn_decode_fused(float *state, int64_t state_seq_stride,
+                            float *conv_state, int64_t conv_seq_stride, float *conv_state_out,
+                            const float *x, int64_t x_stride,
+                            const float *conv_weight, int32_t taps,
+                            const float *br, const float *ar, int64_t gate_stride,
+                            const float *dt_bias, const float *decay_rate, float l2_eps,
+                            const float *z, int64_t z_stride, const float *norm_weight, float eps,
+                            float *out, int64_t out_stride,
+                            int32_t batch, int32_t num_k_heads, int32_t num_v_heads,
+                            int32_t k_dim, int32_t v_dim, void *stream);
+
+/*
  * State pool converters: n elements, fp32 -> binary16 with round to
  * nearest-even (subnormals kept, overflow to infinity, NaN stays NaN), and
  * binary16 -> fp32 (exact).  src and dst must not overlap (an in-place

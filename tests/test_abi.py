@@ -33,7 +33,7 @@ def _declared():
 def test_header_declarations_found():
     names = _declared()
     assert "gdn_decode" in names and "gdn_decode_verify" in names
-    assert len(names) == 10, names
+    assert len(names) == 11, names
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -201,6 +201,48 @@ def test_norm_q_validation(lib):
     assert normq(lib, scales=p["q"], **big) == 5                       # scales over an input
     assert normq(lib, out=None, z=None, **big) == 1                    # z is required
     assert normq(lib, B=0, **big) == 0
+
+
+def fused(lib, **kw):
+    p = _bases()
+    C = (2 * NK + NV) * D
+    a = dict(state=p["state"], pitch=SLOT, ring=p["inter"], rs=4 * C, x=p["q"], xs=C, w=p["k"],
+             taps=4, br=p["alpha"], ar=p["beta"], gs=NV, dt=p["gn"], rate=p["gn"] + 4096,
+             l2=1e-6, z=None, zs=0, gn=None, eps=1e-6, out=p["out"], os=NV * D, B=B, nk=NK, nv=NV,
+             dk=D, dv=D)
+    a.update(kw)
+    return lib.gdn_decode_fused(a["state"], a["pitch"], a["ring"], a["rs"], a.get("rout"), a["x"],
+                                a["xs"], a["w"],
+                                a["taps"], a["br"], a["ar"], a["gs"], a["dt"], a["rate"], a["l2"],
+                                a["z"], a["zs"], a["gn"], a["eps"], a["out"], a["os"], a["B"],
+                                a["nk"], a["nv"], a["dk"], a["dv"], None)
+
+
+def test_fused_validation(lib):
+    p = _bases()
+    C = (2 * NK + NV) * D
+    assert fused(lib, taps=0) == 2
+    assert fused(lib, taps=9) == 2
+    assert fused(lib, nv=3) == 2
+    assert fused(lib, dk=12, dv=12) == 4
+    assert fused(lib, nk=1, nv=64, dk=256, dv=256) == 4     # LDS features above 64 KiB
+    assert fused(lib, l2=-1.0) == 8
+    assert fused(lib, l2=float("nan")) == 8
+    assert fused(lib, ring=None) == 1
+    assert fused(lib, rate=None) == 1
+    assert fused(lib, z=p["z"]) == 1                         # z without norm weight
+    assert fused(lib, rs=4 * C - 4) == 3                     # ring slots overlap
+    assert fused(lib, xs=C - 4) == 3
+    assert fused(lib, ring=p["inter"] + 8) == 3              # misaligned ring
+    assert fused(lib, w=p["k"] + 4) == 3
+    assert fused(lib, ring=p["state"] + 64) == 5             # ring inside the state
+    assert fused(lib, out=p["q"] + 16) == 5                  # output over x
+    assert fused(lib, ring=p["k"] - 16) == 5                 # ring runs into the weights
+    assert fused(lib, rout=p["inter"] + 64) == 5             # new ring over the old one
+    assert fused(lib, rout=p["out"]) == 5                    # new ring over the output
+    assert fused(lib, rout=p["inter"] + (1 << 20) + 4) == 3  # misaligned new ring
+    assert fused(lib, nk=1, nv=64, dk=256, dv=256, rout=p["inter"] + (1 << 20)) != 4
+    assert fused(lib, B=0) == 0
 
 
 def test_converter_validation(lib):
