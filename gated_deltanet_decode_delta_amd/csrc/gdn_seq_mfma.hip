@@ -51,22 +51,6 @@ __device__ __forceinline__ f32x4 mfma(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// inclusive prefix / suffix products over one 16-lane DPP row
-__device__ __forceinline__ float dpp_mul(float x, int ctrl_sel) {
-    int r;
-    switch (ctrl_sel) {
-        case 0: r = __builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(x), 0x111, 0xF, 0xF, false); break;
-        case 1: r = __builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(x), 0x112, 0xF, 0xF, false); break;
-        case 2: r = __builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(x), 0x114, 0xF, 0xF, false); break;
-        case 3: r = __builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(x), 0x118, 0xF, 0xF, false); break;
-        case 4: r = __builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(x), 0x101, 0xF, 0xF, false); break;
-        case 5: r = __builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(x), 0x102, 0xF, 0xF, false); break;
-        case 6: r = __builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(x), 0x104, 0xF, 0xF, false); break;
-        default: r = __builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(x), 0x108, 0xF, 0xF, false); break;
-    }
-    return __int_as_float(r);
-}
-
 }  // namespace
 
 template <bool NORM>
@@ -157,37 +141,41 @@ __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
             kt_s[(col + 2) * kTS + t] = pk[u].z;
             kt_s[(col + 3) * kTS + t] = pk[u].w;
         }
-        if (tid < kC) {   // lanes 0..15 of wave 0: one DPP row
+        if (tid < kC) {
             al_s[tid] = pal;
             be_s[tid] = pbe;
-            float pre = pal;   // P_t = alpha_0 ... alpha_t
-            pre *= dpp_mul(pre, 0);
-            pre *= dpp_mul(pre, 1);
-            pre *= dpp_mul(pre, 2);
-            pre *= dpp_mul(pre, 3);
-            p_s[tid] = pre;
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            // lane s: column s of the range products M[t][s] = alpha_{s+1} ... alpha_t
+        }
+    };
+
+    // Waves 4..7, one thread per (t, s): the range products M[t][s] = alpha_{s+1}
+    // ... alpha_t of the staged chunk (0 above the diagonal), its transpose, the
+    // last row D[s] = M[15][s] and the prefix products P_t = alpha_0 M[t][0].
+    // Each product runs over u = s+1 .. t in increasing order, with no division,
+    // so any alpha >= 0 (zero included) is exact to fp32 rounding.
+    auto range_products = [&]() {
+        if (w >= kWaves - 4) {
+            const int e = tid - (kWaves - 4) * 64;   // 0 .. 255
+            const int t = e >> 4, s = e & 15;
             f32x4 alv[4];
 #pragma unroll
             for (int x4 = 0; x4 < 4; ++x4) alv[x4] = *reinterpret_cast<const f32x4 *>(&al_s[4 * x4]);
-            const int s = tid;
-            float mts = 1.0f;
+            float m = 1.0f;
 #pragma unroll
-            for (int t = 0; t < kC; ++t) {
-                if (t > s) mts *= alv[t >> 2][t & 3];
-                const float v = t >= s ? mts : 0.0f;
-                m_s[t * kTS + s] = v;
-                mt_s[s * kTS + t] = v;
-            }
-            d_s[s] = mts;   // M[15][s]
+            for (int u = 1; u < kC; ++u)
+                if (u > s && u <= t) m *= alv[u >> 2][u & 3];
+            const float v = t >= s ? m : 0.0f;
+            m_s[t * kTS + s] = v;
+            mt_s[s * kTS + t] = v;
+            if (t == kC - 1) d_s[s] = v;
+            if (s == 0) p_s[t] = alv[0][0] * v;
         }
     };
 
     // waves 0..3 (one per SIMD) form a quarter each of the chunk's k.k and k.q
-    // products (columns 32w .. 32w + 31); the quarters are summed when read
+    // products (columns 32w .. 32w + 31); the quarters are summed when read.
+    // Waves 4..7 form the range products meanwhile.
     auto partials = [&]() {
+        range_products();
         if (w < kPartWaves) {
             f32x4 KK = f32x4{0.f, 0.f, 0.f, 0.f}, KQ = KK;
 #pragma unroll
