@@ -371,6 +371,65 @@ def cpu_baseline(seconds: float):
             "tokens_per_s_batch": round(B * calls / el, 1)}
 
 
+def cpu_extras(seconds: float):
+    """The oracle beside each extra workload, each on a bounded sample (about
+    ``seconds`` of host time): binary16-state decode, the 4096-token sequence,
+    the fused input stage and the two-token verify.  Rates use the same
+    formulas as the GPU figures."""
+    import oracle
+    from gated_deltanet_decode_delta_amd import inputs
+
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    res = {}
+
+    def repeat(fn):
+        n, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds or n >= 100:
+                return n, el
+
+    # binary16 state: 16 of the 256 sequences (768 heads) per repetition
+    c = inputs.config_case("fp16_state", B=16)
+    st16 = oracle.f32_to_f16_bits(c.state)
+    heads = [(b, h) for b in range(c.B) for h in range(c.NV)]
+    n, el = repeat(lambda: oracle.seq_head_threaded(
+        st16, c.q, c.k, c.v, c.alpha, c.beta, B=c.B, T=1, NK=c.NK, NV=c.NV, Dk=c.D, Dv=c.D, z=c.z,
+        gn=c.gn, eps=c.eps, heads=heads, threads=threads, state_kind=oracle.STATE_F16))
+    res["fp16_state"] = {"state_GBps": round(2.0 * len(heads) * c.D * c.D * 2 * n / el / 1e9, 3),
+                         "cores": threads, "sample": f"{n} x 768 heads in {el:.1f} s"}
+    # sequence: 2 x threads heads over all 4096 tokens
+    c = inputs.config_case("sequence")
+    heads = [(b, h) for b in range(c.B) for h in range(c.NV)][:2 * threads]
+    st = c.state.copy()
+    t0 = time.perf_counter()
+    oracle.seq_head_threaded(st, c.q, c.k, c.v, c.alpha, c.beta, B=c.B, T=c.T, NK=c.NK, NV=c.NV,
+                             Dk=c.D, Dv=c.D, heads=heads, threads=threads)
+    el = time.perf_counter() - t0
+    res["sequence"] = {"gflops": round(7.0 * c.D * c.D * c.T * len(heads) / el / 1e9, 3),
+                       "cores": threads,
+                       "sample": f"{len(heads)} heads x {c.T} tokens in {el:.1f} s"}
+    # fused input stage: 2 sequences of the B=64 workload, one thread
+    c = inputs.make_frontend_case(3200, B=2, NK=16, NV=48, D=128, taps=4)
+    st, ring = c.state.copy(), c.ring.copy()
+    n, el = repeat(lambda: oracle.fused_decode(st, ring, c.x, c.w, c.br, c.ar, c.dt, c.rate, B=2,
+                                               NK=16, NV=48, D=128, taps=4, z=c.z, gn=c.gn))
+    res["fused"] = {"state_GBps": round(2.0 * 2 * 48 * 128 * 128 * 4 * n / el / 1e9, 3), "cores": 1,
+                    "sample": f"{n} x 2 sequences in {el:.1f} s"}
+    # two-token verify: 4 sequences x 48 heads, threaded
+    c = inputs.make_case(3102, B=4, NK=16, NV=48, D=128, T=2)
+    heads = [(b, h) for b in range(c.B) for h in range(c.NV)]
+    st = c.state.copy()
+    n, el = repeat(lambda: oracle.seq_head_threaded(
+        st, c.q, c.k, c.v, c.alpha, c.beta, B=c.B, T=2, NK=c.NK, NV=c.NV, Dk=c.D, Dv=c.D, z=c.z,
+        gn=c.gn, eps=c.eps, heads=heads, threads=threads))
+    res["verify"] = {"ms_per_call_B64_T2": round(el / n * 16 * 1e3, 2), "cores": threads,
+                     "sample": f"{n} x 4 sequences (T=2) in {el:.1f} s, scaled to B=64"}
+    return res
+
+
 def pmc_traffic(algo_bytes: float):
     """HBM bytes per launch from the committed rocprofv3 counter runs, if they
     were taken on the current kernel sources."""
@@ -516,6 +575,10 @@ def main():
     for w in wanted:
         extra[w] = runners[w]()
     cpu = None if args.no_cpu else cpu_baseline(args.cpu_seconds)
+    if not args.no_cpu and wanted:
+        for name, rate in cpu_extras(args.cpu_seconds / 5).items():
+            if name in extra:
+                extra[name]["cpu_oracle"] = rate
     line = {
         "metric": "GDN decode state GB/s and % HBM roofline; tokens/s·batch at HV=48,D=128",
         "value": round(value, 1),
