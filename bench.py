@@ -475,7 +475,7 @@ def pmc_summarize(fetch_csv: str, write_csv: str):
         return vals
 
     fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
-    name = "void gdn::decode_kernel<128, float, 1>(gdn::StepArgs)"
+    name = "void gdn::decode_kernel<128, float, 1, 16>(gdn::StepArgs)"
     copy = "__amd_rocclr_copyBuffer"
     nbytes = float(1 << 30)
     # the 1 GiB copy is the largest copy dispatch of the run (torch's set-up
@@ -601,7 +601,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": pmc_traffic(m["algo_bytes"]),
-                     "kernel": "gdn::decode_kernel<128, float, kOutNormF32>",
+                     "kernel": "gdn::decode_kernel<128, float, kOutNormF32, 16>",
                      "algorithmic_bytes_per_launch": int(m["algo_bytes"])},
         "cpu_baseline": cpu,
         "extra": extra,

@@ -22,14 +22,17 @@ struct VecT {
     typedef T type __attribute__((ext_vector_type(N)));
 };
 
-template <int D, typename ST>
+// VPL: state values per lane the workgroup size aims at (the workgroup has
+// D*D/VPL threads, clamped to [64, 1024]); fewer values per lane mean more
+// waves per tile and fewer registers per wave.
+template <int D, typename ST, int VPL = 64>
 struct DecodeTile {
     static constexpr int kMaxVec = 16 / (int)sizeof(ST);
     static constexpr int VEC = kMaxVec < D ? kMaxVec : D;     // state elements per vector access
     static constexpr int LPR = (D / VEC) < 16 ? D / VEC : 16; // lanes per row
     static constexpr int NCH = D / (LPR * VEC);               // vectors per lane per row
     static constexpr int C = NCH * VEC;                       // columns per lane
-    static constexpr int NT_RAW = D * D / 64;                 // aim: 64 state values per lane
+    static constexpr int NT_RAW = D * D / VPL;
     static constexpr int NT = NT_RAW < 64 ? 64 : (NT_RAW > 1024 ? 1024 : NT_RAW);
     static constexpr int NG = NT / LPR;                       // row groups
     static constexpr int RPL = (D / NG) < 1 ? 1 : D / NG;     // rows per lane

@@ -361,6 +361,56 @@ def test_every_head_dim_all_entry_points(g, D, NV, NK):
 
 
 # ------------------------------------------------------------- special cases
+@pytest.mark.parametrize("D", [4, 8, 16, 32, 64, 128, 256])
+def test_wide_launch_every_head_dim(g, D):
+    """Launches of 256 or more workgroups use the wide single-token tile (16
+    values per lane for fp32, 32 for binary16); smaller ones the 256-thread
+    tile.  Every decode mode at every D on a wide launch (B=32, NV=8, NK=4)."""
+    import torch
+    B, NK, NV = 32, 4, 8
+    c = inputs.make_case(1100 + D, B=B, NK=NK, NV=NV, D=D)
+    say("wide launch", D)
+    d = _dev_case(c)
+    ref_st = c.state.copy()
+    o_ref = orc.decode(ref_st, c.q, c.k, c.v, c.alpha, c.beta, B=B, NK=NK, NV=NV, Dk=D, Dv=D)
+    y_ref = orc.decode(c.state.copy(), c.q, c.k, c.v, c.alpha, c.beta, B=B, NK=NK, NV=NV, Dk=D,
+                       Dv=D, z=c.z, gn=c.gn, eps=c.eps)
+    st = dev(c.state)
+    o = g.gdn_decode(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"], num_k_heads=NK,
+                     num_v_heads=NV, head_dim=D)
+    assert out_err(host(o), o_ref, NV, D) < TOL_STEP
+    assert tile_err(host(st), ref_st, NV, D) < TOL_STEP
+    for dt in (torch.float32, torch.bfloat16):
+        st = dev(c.state)
+        y = g.gdn_decode_norm(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["z"], d["gn"],
+                              c.eps, out_dtype=dt, num_k_heads=NK, num_v_heads=NV)
+        if dt == torch.float32:
+            assert out_err(host(y), y_ref, NV, D) < TOL_STEP
+        else:
+            assert bf16_ok(host(y), y_ref, NV, D, TOL_STEP) <= 1.0
+        assert tile_err(host(st), ref_st, NV, D) < TOL_STEP
+    if D % 32 == 0:
+        st = dev(c.state)
+        y, codes, scales = g.gdn_decode_norm_q(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                                               d["z"], d["gn"], c.eps, num_k_heads=NK,
+                                               num_v_heads=NV)
+        assert out_err(host(y), y_ref, NV, D) < TOL_STEP
+        yh, ch, sh = host(y), host(codes), host(scales)
+        am = np.abs(yh.reshape(-1, 32)).max(axis=1)
+        want = np.where(am > 0, am / np.float32(127.0), np.float32(1.0)).astype(np.float32)
+        assert np.array_equal(sh.reshape(-1), want)
+        assert np.array_equal(ch.reshape(-1, 32), np.rint(yh.reshape(-1, 32) / want[:, None]).astype(np.int8))
+    st16 = g.gdn_state_f32_to_f16(dev(c.state))
+    ref16 = orc.f32_to_f16_bits(c.state)
+    y16_ref = orc.decode(ref16, c.q, c.k, c.v, c.alpha, c.beta, B=B, NK=NK, NV=NV, Dk=D, Dv=D,
+                         z=c.z, gn=c.gn, eps=c.eps, state_kind=orc.STATE_F16)
+    y16 = g.gdn_decode_f16state(st16, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["z"], d["gn"],
+                                c.eps, out_dtype=torch.float32, num_k_heads=NK, num_v_heads=NV)
+    assert out_err(host(y16), y16_ref, NV, D) < TOL_F16
+    got16 = host(st16).view(np.float16).astype(np.float64)
+    assert tile_err(got16, ref16.view(np.float16).astype(np.float64), NV, D) < TOL_F16
+
+
 def test_pins_hold_on_gpu(g):
     """The closed-form cases of the oracle pins, on the GPU kernels:
     alpha=1/beta=0 leaves the state bit-identical; alpha=0/beta=1 writes v k^T;
