@@ -33,7 +33,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector (packed FMA)
 PMC_FILE = os.path.join(ROOT, "profiles", "decode_norm_b64_pmc.json")
-KERNEL_SOURCES = ("gdn_decode.hip", "gdn_device.h", "gdn_launch.h")
+KERNEL_SOURCES = ("gdn_decode.hip", "gdn_tile.h", "gdn_device.h", "gdn_launch.h")
 
 
 def log(*a):
