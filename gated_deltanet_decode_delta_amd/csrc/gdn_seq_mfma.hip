@@ -54,6 +54,15 @@ __device__ __forceinline__ f32x4 mfma(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// The value of the lane N places higher in the same 16-lane DPP row (row_shl),
+// or 1 past the end of the row.
+template <int N>
+__device__ __forceinline__ float dpp_from_above(float x) {
+    static_assert(N == 1 || N == 2 || N == 4 || N == 8, "row shift");
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(x), 0x100 + N,
+                                                      0xF, 0xF, false));
+}
+
 }  // namespace
 
 template <bool NORM>
@@ -94,7 +103,39 @@ __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
     float4 pk[kPieces], pq[kPieces];
     float pv[4], pz[4];
     float pal = 1.0f, pbe = 0.0f;
+    // element offsets of this lane's prefetch rows at t0 = 0: k/q piece u is
+    // token f >> 5, columns (f & 31) * 4 .. +3 (f = tid + 512u); v and z are the
+    // lane's column of tokens 4g .. 4g + 3
+    int64_t kq_off[kPieces];
+#pragma unroll
+    for (int u = 0; u < kPieces; ++u) {
+        const int f = tid + kThreads * u;
+        kq_off[u] = (row_base + (f >> 5)) * a.qk_stride + (int64_t)kh * kD + (f & 31) * 4;
+    }
+    const int64_t v_off = (row_base + 4 * g) * a.v_stride + vcol;
+    const int64_t z_off = NORM ? (row_base + 4 * g) * a.z_stride + vcol : 0;
     auto prefetch = [&](int t0) {
+        if (t0 + kC <= T) {   // a whole chunk: uniform row offsets, nothing to clamp
+            const int64_t dqk = (int64_t)t0 * a.qk_stride;
+#pragma unroll
+            for (int u = 0; u < kPieces; ++u) {
+                pk[u] = *reinterpret_cast<const float4 *>(a.k + kq_off[u] + dqk);
+                pq[u] = *reinterpret_cast<const float4 *>(a.q + kq_off[u] + dqk);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                pv[r] = a.v[v_off + (int64_t)(t0 + r) * a.v_stride];
+                pz[r] = NORM ? a.z[z_off + (int64_t)(t0 + r) * a.z_stride] : 0.f;
+            }
+            pal = 1.0f;
+            pbe = 0.0f;
+            if (tid < kC) {
+                const int64_t rr = row_base + t0 + tid;
+                pal = a.alpha[rr * a.ab_stride + h];
+                pbe = a.beta[rr * a.ab_stride + h];
+            }
+            return;
+        }
         // Padding tokens (past T): alpha 1, beta 0 and zero k/q/v leave the
         // state and every real token unchanged.  Their loads read row T-1
         // (always valid) and are zeroed by a select, so no load is predicated.
@@ -147,27 +188,27 @@ __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
         }
     };
 
-    // Waves 4..7, one thread per (t, s): the range products M[t][s] = alpha_{s+1}
-    // ... alpha_t of the staged chunk (0 above the diagonal), its transpose, the
-    // last row D[s] = M[15][s] and the prefix products P_t = alpha_0 M[t][0].
-    // Each product runs over u = s+1 .. t in increasing order, with no division,
-    // so any alpha >= 0 (zero included) is exact to fp32 rounding.
+    // Waves 4..7, one thread per (t, s) with s the lane's place in its 16-lane
+    // DPP row: the range products M[t][s] = alpha_{s+1} ... alpha_t of the
+    // staged chunk (0 above the diagonal), its transpose, the last row D[s] =
+    // M[15][s] and the prefix products P_t = alpha_0 M[t][0].  With x_s =
+    // alpha_{s+1} for s < t (else 1), M[t][s] is the suffix product x_s ...
+    // x_15 along the row: four DPP row shifts.  No division, so any alpha >= 0
+    // (zero included) is exact to fp32 rounding.
     auto range_products = [&](int buf) {
         if (w >= kWaves - 4) {
             const int e = tid - (kWaves - 4) * 64;   // 0 .. 255
             const int t = e >> 4, s = e & 15;
-            f32x4 alv[4];
-#pragma unroll
-            for (int x4 = 0; x4 < 4; ++x4) alv[x4] = *reinterpret_cast<const f32x4 *>(&al_s[buf][4 * x4]);
-            float m = 1.0f;
-#pragma unroll
-            for (int u = 1; u < kC; ++u)
-                if (u > s && u <= t) m *= alv[u >> 2][u & 3];
+            float m = s < t ? al_s[buf][s + 1] : 1.0f;
+            m *= dpp_from_above<1>(m);
+            m *= dpp_from_above<2>(m);
+            m *= dpp_from_above<4>(m);
+            m *= dpp_from_above<8>(m);
             const float v = t >= s ? m : 0.0f;
             m_s[t * kTS + s] = v;
             mt_s[s * kTS + t] = v;
             if (t == kC - 1) d_s[buf][s] = v;
-            if (s == 0) p_s[buf][t] = alv[0][0] * v;
+            if (s == 0) p_s[buf][t] = al_s[buf][0] * v;
         }
     };
 
@@ -194,6 +235,9 @@ __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
         }
     };
 
+    float unit[kC];   // column li of the identity (the solve's right-hand side)
+#pragma unroll
+    for (int t = 0; t < kC; ++t) unit[t] = t == li ? 1.0f : 0.0f;
     float vcur[4], zcur[4], vnxt[4], znxt[4];
     prefetch(0);
     stage(0);
@@ -249,6 +293,8 @@ __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
             }
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
             __builtin_amdgcn_wave_barrier();
+            // x = column li of T: x[t] = [t == li] - sum_{s<t} A[t][s] x[s]; the
+            // entries above li come out exactly 0 and x[li] exactly 1
             float x[kC];
 #pragma unroll
             for (int t = 0; t < kC; ++t) x[t] = 0.0f;
@@ -263,7 +309,7 @@ __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
                     acc0 = fmaf(av[2], x[4 * s4 + 2], acc0);
                     acc1 = fmaf(av[3], x[4 * s4 + 3], acc1);
                 }
-                x[t] = t < li ? 0.0f : (t == li ? 1.0f : -(acc0 + acc1));
+                x[t] = unit[t] - (acc0 + acc1);
             }
             if (g == 0) {
 #pragma unroll
