@@ -5,11 +5,13 @@
 // so each state slot is read once at the start and written once at the end,
 // whatever the sequence length.
 //
+// This token loop serves every head dim except D = 128, which launch_seq sends
+// to the chunked matrix-core kernel of gdn_seq_mfma.hip.
+//
 // Mapping (gfx950).  Rows of a head's state are independent given the head's
 // per-token k, q, alpha and beta, so without the fused norm a head is split
-// over RB workgroups of D/RB rows each (RB = 4 at D = 128: 768 workgroups of 4
-// waves for the 4 x 48-head workload, three waves per SIMD on 256 CUs).  With
-// the norm a workgroup owns the whole head.  Row i is held by L = 8 lanes, each
+// over RB workgroups of D/RB rows each (RB = 4 for D >= 64).  With the norm a
+// workgroup owns the whole head.  Row i is held by L = 8 lanes, each
 // keeping D/8 of its columns in VGPRs; S_i.k and S_i.q are in-row DPP
 // all-reductions, so no barrier is needed per token.  The lanes of a row own
 // 16-byte column pieces interleaved across the row, so each per-token LDS read
