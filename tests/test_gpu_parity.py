@@ -612,3 +612,51 @@ def test_graph_replay_matches_eager(g):
         for l in range(L):
             assert torch.equal(out_g[l], out_e[l]), (rep, l)
             assert torch.equal(st_g[l], st_e[l]), (rep, l)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 32, 33, 48])
+@pytest.mark.parametrize("norm", [False, True])
+def test_sequence_chunk_boundaries(g, D, T, norm):
+    """Lengths around the 16-token chunk (and the two chunk buffers of the
+    matrix-core kernel at D = 128): outputs and final state against the oracle."""
+    B, NK, NV = 2, 2, 6
+    c = inputs.make_case(1300 + T + D, B=B, NK=NK, NV=NV, D=D, T=T)
+    say("seq boundary", D, T, norm)
+    d = _dev_case(c)
+    st = dev(c.state)
+    kw = dict(z=d["z"], norm_weight=d["gn"], eps=c.eps) if norm else dict(head_dim=D)
+    o = g.gdn_recurrence_seq(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"], seq_len=T,
+                             num_k_heads=NK, num_v_heads=NV, **kw)
+    ref_st = c.state.copy()
+    okw = dict(z=c.z, gn=c.gn, eps=c.eps) if norm else {}
+    ref = orc.seq(ref_st, c.q, c.k, c.v, c.alpha, c.beta, B=B, T=T, NK=NK, NV=NV, Dk=D, Dv=D, **okw)
+    assert out_err(host(o), ref, NV, D) < TOL_CHAIN
+    assert tile_err(host(st), ref_st, NV, D) < TOL_CHAIN
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_sequence_extreme_decay(g, D):
+    """Decays of exactly 0 (the state is forgotten), 1e-8 (the running decay
+    product leaves any fixed exponent range within a few tokens), 1 (no decay)
+    and ordinary values, mixed within chunks, with write strengths of 0 and 1
+    among them: outputs and final state against the oracle."""
+    B, NK, NV, T = 2, 2, 4, 100
+    c = inputs.make_case(1400 + D, B=B, NK=NK, NV=NV, D=D, T=T)
+    r = np.random.Generator(np.random.PCG64(1401))
+    pick = r.integers(0, 5, size=c.alpha.shape)
+    c.alpha[:] = np.choose(pick, [np.float32(0.0), np.float32(1e-8), np.float32(1.0),
+                                  np.float32(0.5), c.alpha]).astype(np.float32)
+    c.beta[r.random(c.beta.shape) < 0.2] = 0.0
+    c.beta[r.random(c.beta.shape) < 0.2] = 1.0
+    say("seq extreme decay", D)
+    d = _dev_case(c)
+    st = dev(c.state)
+    o = g.gdn_recurrence_seq(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"], seq_len=T,
+                             num_k_heads=NK, num_v_heads=NV, head_dim=D)
+    ref_st = c.state.copy()
+    ref = orc.seq(ref_st, c.q, c.k, c.v, c.alpha, c.beta, B=B, T=T, NK=NK, NV=NV, Dk=D, Dv=D)
+    got_o, got_st = host(o), host(st)
+    assert np.isfinite(got_o).all() and np.isfinite(got_st).all()
+    assert out_err(got_o, ref, NV, D) < TOL_CHAIN
+    assert tile_err(got_st, ref_st, NV, D) < TOL_CHAIN
