@@ -660,3 +660,31 @@ def test_sequence_extreme_decay(g, D):
     assert np.isfinite(got_o).all() and np.isfinite(got_st).all()
     assert out_err(got_o, ref, NV, D) < TOL_CHAIN
     assert tile_err(got_st, ref_st, NV, D) < TOL_CHAIN
+
+
+def test_calls_on_side_streams(g):
+    """Calls run on the stream they are given: two pools advanced concurrently
+    on two side streams (disjoint state and outputs) match the oracle, and an
+    explicit stream handle works like the current-stream default."""
+    import torch
+    B, NK, NV, D = 8, 4, 8, 128
+    ca = inputs.make_case(1500, B=B, NK=NK, NV=NV, D=D)
+    cb = inputs.make_case(1501, B=B, NK=NK, NV=NV, D=D)
+    say("side streams")
+    da, db = _dev_case(ca), _dev_case(cb)
+    sta, stb = dev(ca.state), dev(cb.state)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s1):
+        ya = g.gdn_decode_norm(sta, da["q"], da["k"], da["v"], da["alpha"], da["beta"], da["z"],
+                               da["gn"], ca.eps, num_k_heads=NK, num_v_heads=NV)
+    yb = g.gdn_decode_norm(stb, db["q"], db["k"], db["v"], db["alpha"], db["beta"], db["z"],
+                           db["gn"], cb.eps, num_k_heads=NK, num_v_heads=NV,
+                           stream=s2.cuda_stream)
+    torch.cuda.synchronize()
+    for c, y, st in ((ca, ya, sta), (cb, yb, stb)):
+        ref_st = c.state.copy()
+        ref = orc.decode(ref_st, c.q, c.k, c.v, c.alpha, c.beta, B=B, NK=NK, NV=NV, Dk=D, Dv=D,
+                         z=c.z, gn=c.gn, eps=c.eps)
+        assert out_err(host(y), ref, NV, D) < TOL_STEP
+        assert tile_err(host(st), ref_st, NV, D) < TOL_STEP
