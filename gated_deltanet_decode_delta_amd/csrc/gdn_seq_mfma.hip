@@ -127,10 +127,8 @@ __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
                 pv[r] = a.v[v_off + (int64_t)(t0 + r) * a.v_stride];
                 pz[r] = NORM ? a.z[z_off + (int64_t)(t0 + r) * a.z_stride] : 0.f;
             }
-            pal = 1.0f;
-            pbe = 0.0f;
-            if (tid < kC) {
-                const int64_t rr = row_base + t0 + tid;
+            {   // every lane loads (token tid % 16): no divergent branch among the loads
+                const int64_t rr = row_base + t0 + (tid & (kC - 1));
                 pal = a.alpha[rr * a.ab_stride + h];
                 pbe = a.beta[rr * a.ab_stride + h];
             }
@@ -257,7 +255,7 @@ __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
     // Per chunk c (buffer cur = c & 1), two barriers:
     //   T(c) and U, W on the matrix cores; chunk c+1 staged into the other buffer
     //   -- barrier: T(c) and chunk c+1 visible --
-    //   prefetch of chunk c+2; C', O, outputs, state update; chunk c+1's k.k,
+    //   C', O, outputs, state update; prefetch of chunk c+2; chunk c+1's k.k,
     //   k.q partials and range products
     //   -- barrier: chunk c+1 prepared, every read of chunk c done --
     float *outp = static_cast<float *>(a.out);
@@ -342,7 +340,6 @@ __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
             }
         }
         __syncthreads();   // T(c) visible to every wave; chunk c+1 staged
-        if (t0 + 2 * kC < T) prefetch(t0 + 2 * kC);
 
         const f32x4 Ta = *reinterpret_cast<const f32x4 *>(&t_s[li * kTS + 4 * g]);
         const f32x4 Pt = *reinterpret_cast<const f32x4 *>(&p_s[cur][4 * g]);
@@ -423,6 +420,9 @@ __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
 #pragma unroll
             for (int m = 0; m < 8; ++m) S[m] = mfma(kc[s4 * kKS + 16 * m], Cp[s4], S[m]);
 
+        // chunk c+2's loads go out after this chunk's output stores: the wait for
+        // them (at the next staging) then never waits on a store issued later
+        if (t0 + 2 * kC < T) prefetch(t0 + 2 * kC);
         if (has_next) partials(cur ^ 1);
         __syncthreads();   // chunk c+1 prepared; every read of chunk c is done
 #pragma unroll
