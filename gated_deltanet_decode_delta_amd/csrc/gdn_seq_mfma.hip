@@ -372,7 +372,8 @@ __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 4 * g + r;
-                if (t < nt) outp[(row_base + t0 + t) * a.out_stride + vcol] = O[r] * a.scale;
+                // a whole chunk stores without per-token branches
+                if (nt == kC || t < nt) outp[(row_base + t0 + t) * a.out_stride + vcol] = O[r] * a.scale;
             }
         } else {
 #pragma unroll
@@ -389,7 +390,7 @@ __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
 #pragma unroll
                 for (int v2 = 0; v2 < kWaves; ++v2) tot += nrm_s[v2][t];
                 const float rr_ = sqrtf(tot * (1.0f / kD) + a.eps);
-                if (t < nt) {
+                if (nt == kC || t < nt) {
                     const float o = O[r] * a.scale;
                     outp[(row_base + t0 + t) * a.out_stride + vcol] = (gnv * o / rr_) * silu(zcur[r]);
                 }
