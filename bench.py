@@ -364,11 +364,17 @@ def cpu_baseline(seconds: float):
         if el >= seconds or calls >= 200:
             break
     state_bytes = 2.0 * B * NV * D * D * 4 * calls
+    # the same oracle on one thread, one whole call
+    t1 = time.perf_counter()
+    oracle.decode(st, c.q, c.k, c.v, c.alpha, c.beta, B=B, NK=NK, NV=NV, Dk=D, Dv=D, z=c.z,
+                  gn=c.gn, eps=c.eps)
+    el1 = time.perf_counter() - t1
     return {"value": round(state_bytes / el / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{calls} full B=64 gdn_decode_norm calls (3072 heads each) in {el:.1f} s "
                       f"on {threads} host threads; state GB/s by the same formula",
-            "tokens_per_s_batch": round(B * calls / el, 1)}
+            "tokens_per_s_batch": round(B * calls / el, 1),
+            "single_thread_GBps": round(2.0 * B * NV * D * D * 4 / el1 / 1e9, 3)}
 
 
 def cpu_extras(seconds: float):

@@ -73,6 +73,8 @@ def _load():
     lib.orc_seq_head.argtypes = [i32, i32, i32, i32] + common
     lib.orc_seq.restype = i32
     lib.orc_seq.argtypes = [i32, i32, i32] + common
+    lib.orc_seq_head_list.restype = i32
+    lib.orc_seq_head_list.argtypes = [i32, vp, vp, i32, i32] + common
     f32p = vp
     lib.orc_frontend_token.restype = i32
     lib.orc_frontend_token.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, dbl,
@@ -234,11 +236,17 @@ def seq_head_threaded(state, q, k, v, alpha, beta, *, B, T, NK, NV, Dk, Dv, head
             _row_stride(z) if z is not None else 0, _ptr(gn), float(eps), _ptr(out),
             _row_stride(out), NK, NV, Dk, Dv]
 
-    def run(bh):
-        return lib.orc_seq_head(int(bh[0]), int(bh[1]), T, state_kind, *args)
+    # each thread runs a contiguous share of the heads in one C call
+    hl = np.asarray(heads, dtype=np.int32).reshape(-1, 2)
+    shares = [np.ascontiguousarray(part) for part in np.array_split(hl, max(1, threads)) if len(part)]
+
+    def run(part):
+        bs = np.ascontiguousarray(part[:, 0])
+        hs = np.ascontiguousarray(part[:, 1])
+        return lib.orc_seq_head_list(len(part), _ptr(bs), _ptr(hs), T, state_kind, *args)
 
     with ThreadPoolExecutor(max_workers=threads) as ex:
-        rcs = list(ex.map(run, heads))
+        rcs = list(ex.map(run, shares))
     if any(rcs):
         raise RuntimeError("oracle failed")
     return out

@@ -282,6 +282,26 @@ int orc_seq(int B, int T, int state_kind, void *state, int64_t pitch,
     return 0;
 }
 
+/* A list of (b, h) heads, one after the other (a driver for timing the oracle
+ * on several host threads: each thread takes its own list, and distinct heads
+ * touch disjoint state and output). */
+int orc_seq_head_list(int n, const int *bs, const int *hs, int T, int state_kind, void *state,
+                      int64_t pitch, const float *q, const float *k, int64_t qk_stride,
+                      const float *v, int64_t v_stride,
+                      const float *alpha, const float *beta, int64_t ab_stride,
+                      const float *z, int64_t z_stride, const float *gn, double eps,
+                      double *out, int64_t out_stride,
+                      int NK, int NV, int Dk, int Dv)
+{
+    for (int i = 0; i < n; ++i) {
+        int rc = orc_seq_head(bs[i], hs[i], T, state_kind, state, pitch, q, k, qk_stride, v,
+                              v_stride, alpha, beta, ab_stride, z, z_stride, gn, eps, out,
+                              out_stride, NK, NV, Dk, Dv);
+        if (rc) return rc;
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------------------- */
 /* Front end of the decode step: conv ring, silu, L2 of q and k, the gates.   */
 /* ------------------------------------------------------------------------- */

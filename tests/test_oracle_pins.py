@@ -583,3 +583,20 @@ def test_p16_quant_round_trip_bound(orc):
     top = np.abs(ys).argmax(axis=1)
     assert (np.abs(cs[np.arange(cs.shape[0]), top]) == 127).all()
     np.testing.assert_allclose(sc[:, 0], np.abs(ys).max(axis=1) / 127, rtol=1e-7)
+
+
+def test_threaded_driver_equals_serial(orc):
+    """The multi-threaded timing driver runs the same per-head code: outputs and
+    states equal the serial call bit for bit, for any split of the heads."""
+    c = inputs.make_case(91, B=3, NK=2, NV=4, D=8, T=5)
+    st0 = c.state.copy()
+    ref = orc.seq(st0, c.q, c.k, c.v, c.alpha, c.beta, B=3, T=5, NK=2, NV=4, Dk=8, Dv=8,
+                  z=c.z, gn=c.gn, eps=1e-6)
+    heads = [(b, h) for b in range(3) for h in range(4)]
+    for threads in (1, 3, 5, 12):
+        st = c.state.copy()
+        got = orc.seq_head_threaded(st, c.q, c.k, c.v, c.alpha, c.beta, B=3, T=5, NK=2, NV=4,
+                                    Dk=8, Dv=8, heads=heads, threads=threads, z=c.z, gn=c.gn,
+                                    eps=1e-6)
+        assert np.array_equal(got, ref), threads
+        assert np.array_equal(st, st0), threads
