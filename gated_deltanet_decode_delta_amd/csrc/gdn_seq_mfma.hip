@@ -27,9 +27,11 @@
 // is exactly the B-operand layout of the product K S^T with the contraction
 // index j ordered (m, r, l/16), so the state never moves between the U/W
 // products and the update.  k and q of a chunk are staged in LDS (read once per
-// 16-row tile instead of once per lane), double-buffered so that the next
-// chunk is staged, and its k.k / k.q tiles and range products formed, while
-// this chunk runs: two workgroup barriers per chunk.  v and z go from global
+// 16-row tile instead of once per lane).  The chunk-level quantities run ahead
+// of the state work: during chunk c, chunk c+2 is staged and its k.k / k.q tiles
+// and range products formed, and the triangular inverse of chunk c+1 is
+// solved, so the first half of every chunk is the U / W products alone, equal
+// on every SIMD; two workgroup barriers per chunk.  v and z go from global
 // memory straight to the lanes that use them.
 #include "gdn_device.h"
 #include "gdn_launch.h"
@@ -47,7 +49,9 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kKS = kD + 4;      // row stride (floats) of k_s / q_s
 constexpr int kTS = kC + 4;      // row stride of the 16x16 matrices in LDS
 constexpr int kPieces = kC * kD / 4 / kThreads;   // 16-byte pieces of a chunk's k (or q) per thread
-constexpr int kPartWaves = 4;    // waves forming the chunk's k.k / k.q (two 16-column slices each)
+constexpr int kPartWaves = 3;    // waves 1..3 form the chunk's k.k / k.q (16-column slices 3,3,2)
+constexpr int kSolveWave = 0;    // forms A and solves for T, while waves 1..3 form the k.k / k.q
+constexpr int kBufs = 3;         // chunks c, c+1 and c+2 are staged during chunk c
 static_assert(kPieces * kThreads * 4 == kC * kD, "staging covers the chunk exactly");
 
 __device__ __forceinline__ f32x4 mfma(float a, float b, f32x4 c) {
@@ -67,13 +71,15 @@ __device__ __forceinline__ float dpp_from_above(float x) {
 
 template <bool NORM>
 __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
-    // Chunk data is double-buffered (buffer c & 1 holds chunk c), so the next
-    // chunk is staged and prepared while this one is on the matrix cores.
-    __shared__ __align__(16) float k_s[2][kC * kKS], q_s[2][kC * kKS];
-    __shared__ f32x4 part_s[kPartWaves][2][64];          // partial k.k and k.q tiles
-    __shared__ __align__(16) float a_s[kC * kTS], t_s[kC * kTS];  // A and T = (I + A)^{-1}
-    __shared__ __align__(16) float m_s[kC * kTS], mt_s[kC * kTS]; // M[t][s] and its transpose
-    __shared__ __align__(16) float al_s[2][kC], be_s[2][kC], p_s[2][kC], d_s[2][kC];
+    // Chunk data: buffer c % 3 holds chunk c's k, q, alpha, beta, P and D
+    // (chunks c, c+1, c+2 are live during chunk c); the k.k / k.q partials, M,
+    // M^T and T of chunk c sit in buffer c & 1 (written one or two chunks
+    // ahead, read during chunk c - 1 or c).
+    __shared__ __align__(16) float k_s[kBufs][kC * kKS], q_s[kBufs][kC * kKS];
+    __shared__ f32x4 part_s[2][kPartWaves][2][64];       // partial k.k and k.q tiles
+    __shared__ __align__(16) float a_s[kC * kTS], t_s[2][kC * kTS];  // A and T = (I + A)^{-1}
+    __shared__ __align__(16) float m_s[2][kC * kTS], mt_s[2][kC * kTS]; // M[t][s] and its transpose
+    __shared__ __align__(16) float al_s[kBufs][kC], be_s[kBufs][kC], p_s[kBufs][kC], d_s[kBufs][kC];
     __shared__ float nrm_s[NORM ? kWaves : 1][kC];
 
     const int tid = threadIdx.x;
@@ -193,106 +199,72 @@ __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
     // alpha_{s+1} for s < t (else 1), M[t][s] is the suffix product x_s ...
     // x_15 along the row: four DPP row shifts.  No division, so any alpha >= 0
     // (zero included) is exact to fp32 rounding.
-    auto range_products = [&](int buf) {
+    float unit[kC];   // column li of the identity (the solve's right-hand side)
+#pragma unroll
+    for (int t = 0; t < kC; ++t) unit[t] = t == li ? 1.0f : 0.0f;
+
+    auto range_products = [&](int b3, int par) {
         if (w >= kWaves - 4) {
             const int e = tid - (kWaves - 4) * 64;   // 0 .. 255
             const int t = e >> 4, s = e & 15;
-            float m = s < t ? al_s[buf][s + 1] : 1.0f;
+            float m = s < t ? al_s[b3][s + 1] : 1.0f;
             m *= dpp_from_above<1>(m);
             m *= dpp_from_above<2>(m);
             m *= dpp_from_above<4>(m);
             m *= dpp_from_above<8>(m);
             const float v = t >= s ? m : 0.0f;
-            m_s[t * kTS + s] = v;
-            mt_s[s * kTS + t] = v;
-            if (t == kC - 1) d_s[buf][s] = v;
-            if (s == 0) p_s[buf][t] = al_s[buf][0] * v;
+            m_s[par][t * kTS + s] = v;
+            mt_s[par][s * kTS + t] = v;
+            if (t == kC - 1) d_s[b3][s] = v;
+            if (s == 0) p_s[b3][t] = al_s[b3][0] * v;
         }
     };
 
-    // waves 0..3 (one per SIMD) form a quarter each of the chunk's k.k and k.q
-    // products (columns 32w .. 32w + 31); the quarters are summed when read.
-    // Waves 4..7 form the range products meanwhile.
-    auto partials = [&](int buf) {
-        range_products(buf);
-        if (w < kPartWaves) {
+    // waves 1..3 (SIMDs 1..3) form a part each of the chunk's k.k and k.q
+    // products (16-column slices 3p .. 3p + 2 of the 8); the parts are summed
+    // when read.  Waves 4..7 form the range products meanwhile.
+    auto partials = [&](int b3, int par) {
+        range_products(b3, par);
+        if (w >= 1 && w <= kPartWaves) {
+            const int pw = w - 1;
             f32x4 KK = f32x4{0.f, 0.f, 0.f, 0.f}, KQ = KK;
 #pragma unroll
-            for (int mm = 0; mm < 2; ++mm) {
-                const int m = 2 * w + mm;
-                const f32x4 ka = *reinterpret_cast<const f32x4 *>(&k_s[buf][li * kKS + 16 * m + 4 * g]);
-                const f32x4 qa = *reinterpret_cast<const f32x4 *>(&q_s[buf][li * kKS + 16 * m + 4 * g]);
+            for (int mm = 0; mm < 3; ++mm) {
+                const int m = 3 * pw + mm;
+                if (m < kD / 16) {
+                    const f32x4 ka = *reinterpret_cast<const f32x4 *>(&k_s[b3][li * kKS + 16 * m + 4 * g]);
+                    const f32x4 qa = *reinterpret_cast<const f32x4 *>(&q_s[b3][li * kKS + 16 * m + 4 * g]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    KK = mfma(ka[r], ka[r], KK);   // k_t . k_s
-                    KQ = mfma(ka[r], qa[r], KQ);   // k_t . q_s
+                    for (int r = 0; r < 4; ++r) {
+                        KK = mfma(ka[r], ka[r], KK);   // k_t . k_s
+                        KQ = mfma(ka[r], qa[r], KQ);   // k_t . q_s
+                    }
                 }
             }
-            part_s[w][0][l] = KK;
-            part_s[w][1][l] = KQ;
+            part_s[par][pw][0][l] = KK;
+            part_s[par][pw][1][l] = KQ;
         }
     };
 
-    float unit[kC];   // column li of the identity (the solve's right-hand side)
-#pragma unroll
-    for (int t = 0; t < kC; ++t) unit[t] = t == li ? 1.0f : 0.0f;
-    float vcur[4], zcur[4], vnxt[4], znxt[4];
-    prefetch(0);
-    stage(0);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        vcur[r] = pv[r];
-        zcur[r] = pz[r];
-    }
-    // drain every load (the state included) so that no conservative vmcnt wait
-    // lands inside the chunk loop, where it would also wait for the prefetch
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    partials(0);
-    if (kC < T) prefetch(kC);
-    __syncthreads();
-
-    // Per chunk c (buffer cur = c & 1), two barriers:
-    //   T(c) and U, W on the matrix cores; chunk c+1 staged into the other buffer
-    //   -- barrier: T(c) and chunk c+1 visible --
-    //   C', O, outputs, state update; prefetch of chunk c+2; chunk c+1's k.k,
-    //   k.q partials and range products
-    //   -- barrier: chunk c+1 prepared, every read of chunk c done --
-    float *outp = static_cast<float *>(a.out);
-    for (int t0 = 0, cur = 0; t0 < T; t0 += kC, cur ^= 1) {
-        const bool has_next = t0 + kC < T;
-        const int nt = T - t0 < kC ? T - t0 : kC;
-        // Lane (g, li) owns tile entries (a, b) = (4g + r, li):
-        //   A[a][b] = beta_a M[a][b] (k_a.k_b)  for b < a  (tile layout, for the solve)
-        //   G[b][a] = M[b][a] (q_b.k_a)          for a <= b (MFMA A-operand layout)
-        // k.k is symmetric and k_a.q_b is the tile entry of the k.q product, so
-        // no value moves between lanes.  Every wave forms its own G; wave 0 also
-        // forms A and solves T = (I + A)^{-1} once for the workgroup (lane column
-        // c = li, forward substitution), while the other waves start on U and W.
-        const f32x4 bet = *reinterpret_cast<const f32x4 *>(&be_s[cur][4 * g]);
-        const f32x4 mA = *reinterpret_cast<const f32x4 *>(&mt_s[li * kTS + 4 * g]);   // M[4g+r][li]
-        const f32x4 mG = *reinterpret_cast<const f32x4 *>(&m_s[li * kTS + 4 * g]);    // M[li][4g+r]
-        f32x4 Ga;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float kq = 0.f;
-#pragma unroll
-            for (int v2 = 0; v2 < kPartWaves; ++v2) kq += part_s[v2][1][l][r];
-            Ga[r] = mG[r] * kq;   // M[li][a] is 0 above the diagonal
-        }
-        if (w == 0) {
+    // Wave 0: A[a][b] = beta_a M[a][b] (k_a.k_b) for b < a, then T = (I + A)^{-1}
+    // column by column (lane column li, forward substitution with the identity
+    // column as right-hand side: the entries above li come out exactly 0 and
+    // x[li] exactly 1).  Lane (g, li) owns A[4g + r][li]; k.k is symmetric, so
+    // no value moves between lanes before the LDS round trip.
+    auto solve = [&](int b3, int par) {
+        if (w == kSolveWave) {
+            const f32x4 bet = *reinterpret_cast<const f32x4 *>(&be_s[b3][4 * g]);
+            const f32x4 mA = *reinterpret_cast<const f32x4 *>(&mt_s[par][li * kTS + 4 * g]);  // M[4g+r][li]
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int ai = 4 * g + r;
                 float kk = 0.f;
 #pragma unroll
-                for (int v2 = 0; v2 < kPartWaves; ++v2) kk += part_s[v2][0][l][r];
+                for (int v2 = 0; v2 < kPartWaves; ++v2) kk += part_s[par][v2][0][l][r];
                 a_s[ai * kTS + li] = li < ai ? bet[r] * mA[r] * kk : 0.0f;
             }
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
             __builtin_amdgcn_wave_barrier();
-            // x = column li of T: x[t] = [t == li] - sum_{s<t} A[t][s] x[s]; the
-            // entries above li come out exactly 0 and x[li] exactly 1
             float x[kC];
 #pragma unroll
             for (int t = 0; t < kC; ++t) x[t] = 0.0f;
@@ -311,8 +283,62 @@ __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
             }
             if (g == 0) {
 #pragma unroll
-                for (int t = 0; t < kC; ++t) t_s[t * kTS + li] = x[t];
+                for (int t = 0; t < kC; ++t) t_s[par][t * kTS + li] = x[t];
             }
+        }
+    };
+
+    float vcur[4], zcur[4], vn1[4], zn1[4], vn2[4], zn2[4];
+    auto take = [&](float *vd, float *zd) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            vd[r] = pv[r];
+            zd[r] = pz[r];
+        }
+    };
+    // Prologue: chunk 0 staged and prepared, chunk 1 staged and prepared, T of
+    // chunk 0 solved, chunk 2's loads in flight.
+    prefetch(0);
+    stage(0);
+    take(vcur, zcur);
+    // drain every load (the state included) so that no conservative vmcnt wait
+    // lands inside the chunk loop, where it would also wait for the prefetch
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (kC < T) prefetch(kC);
+    partials(0, 0);
+    if (kC < T) {
+        stage(1);
+        take(vn1, zn1);
+    }
+    __syncthreads();
+    if (2 * kC < T) prefetch(2 * kC);
+    solve(0, 0);
+    if (kC < T) partials(1, 1);
+    __syncthreads();
+
+    // Per chunk c (chunk buffer b3 = c % 3, pair buffer par = c & 1), two barriers:
+    //   U, W on the matrix cores (every wave alike); chunk c+2 staged
+    //   -- barrier: chunk c+2 visible --
+    //   C', O, outputs, state update; prefetch of chunk c+3; chunk c+2's k.k,
+    //   k.q partials and range products; A and T of chunk c+1 (wave 0)
+    //   -- barrier: chunk c+2 prepared, T(c+1) visible, every read of chunk c done --
+    float *outp = static_cast<float *>(a.out);
+    for (int t0 = 0, b3 = 0, par = 0; t0 < T; t0 += kC, b3 = b3 == kBufs - 1 ? 0 : b3 + 1, par ^= 1) {
+        const int b3n1 = b3 == kBufs - 1 ? 0 : b3 + 1;     // buffer of chunk c+1
+        const int b3n2 = b3n1 == kBufs - 1 ? 0 : b3n1 + 1; // buffer of chunk c+2
+        const int nt = T - t0 < kC ? T - t0 : kC;
+        // G[b][a] = M[b][a] (q_b.k_a) for a <= b, lane (g, li) holding a = 4g + r,
+        // b = li (the MFMA A-operand layout of O += G C'); k_a.q_b is the tile
+        // entry of the k.q product, so no value moves between lanes.
+        const f32x4 mG = *reinterpret_cast<const f32x4 *>(&m_s[par][li * kTS + 4 * g]);    // M[li][4g+r]
+        f32x4 Ga;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float kq = 0.f;
+#pragma unroll
+            for (int v2 = 0; v2 < kPartWaves; ++v2) kq += part_s[par][v2][1][l][r];
+            Ga[r] = mG[r] * kq;   // M[li][a] is 0 above the diagonal
         }
 
         // U^T = K S^T and W^T = Q S^T on the matrix cores (four independent
@@ -320,8 +346,8 @@ __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
         f32x4 Ua = f32x4{0.f, 0.f, 0.f, 0.f}, Ub = Ua, Wa = Ua, Wb = Ua;
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
-            const f32x4 ka = *reinterpret_cast<const f32x4 *>(&k_s[cur][li * kKS + 16 * m + 4 * g]);
-            const f32x4 qa = *reinterpret_cast<const f32x4 *>(&q_s[cur][li * kKS + 16 * m + 4 * g]);
+            const f32x4 ka = *reinterpret_cast<const f32x4 *>(&k_s[b3][li * kKS + 16 * m + 4 * g]);
+            const f32x4 qa = *reinterpret_cast<const f32x4 *>(&q_s[b3][li * kKS + 16 * m + 4 * g]);
 #pragma unroll
             for (int r = 0; r < 4; r += 2) {
                 Ua = mfma(ka[r], S[m][r], Ua);
@@ -331,20 +357,17 @@ __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
             }
         }
         const f32x4 U = Ua + Ub, W = Wa + Wb;
-        if (has_next) {
-            stage(cur ^ 1);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                vnxt[r] = pv[r];
-                znxt[r] = pz[r];
-            }
+        if (t0 + 2 * kC < T) {
+            stage(b3n2);
+            take(vn2, zn2);
         }
-        __syncthreads();   // T(c) visible to every wave; chunk c+1 staged
+        __syncthreads();   // chunk c+2 staged
 
-        const f32x4 Ta = *reinterpret_cast<const f32x4 *>(&t_s[li * kTS + 4 * g]);
-        const f32x4 Pt = *reinterpret_cast<const f32x4 *>(&p_s[cur][4 * g]);
-        const f32x4 Dt = *reinterpret_cast<const f32x4 *>(&d_s[cur][4 * g]);
-        const float Plast = p_s[cur][kC - 1];
+        const f32x4 bet = *reinterpret_cast<const f32x4 *>(&be_s[b3][4 * g]);
+        const f32x4 Ta = *reinterpret_cast<const f32x4 *>(&t_s[par][li * kTS + 4 * g]);
+        const f32x4 Pt = *reinterpret_cast<const f32x4 *>(&p_s[b3][4 * g]);
+        const f32x4 Dt = *reinterpret_cast<const f32x4 *>(&d_s[b3][4 * g]);
+        const float Plast = p_s[b3][kC - 1];
 
         // R = beta (v - P gam U);  C' = T R;  O = P gam W + G C'
         f32x4 R, Cp, O;
@@ -415,21 +438,24 @@ __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) Cp[r] *= Dt[r] * cscale;
         // k of token 4g + s4, column 16m + li: the A operand of the update
-        const float *kc = &k_s[cur][4 * g * kKS + li];
+        const float *kc = &k_s[b3][4 * g * kKS + li];
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
             for (int m = 0; m < 8; ++m) S[m] = mfma(kc[s4 * kKS + 16 * m], Cp[s4], S[m]);
 
-        // chunk c+2's loads go out after this chunk's output stores: the wait for
+        // chunk c+3's loads go out after this chunk's output stores: the wait for
         // them (at the next staging) then never waits on a store issued later
-        if (t0 + 2 * kC < T) prefetch(t0 + 2 * kC);
-        if (has_next) partials(cur ^ 1);
-        __syncthreads();   // chunk c+1 prepared; every read of chunk c is done
+        if (t0 + 3 * kC < T) prefetch(t0 + 3 * kC);
+        if (t0 + 2 * kC < T) partials(b3n2, par);   // chunk c+2 uses pair buffer par too
+        if (t0 + kC < T) solve(b3n1, par ^ 1);
+        __syncthreads();   // chunk c+2 prepared; T(c+1) visible; every read of chunk c done
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            vcur[r] = vnxt[r];
-            zcur[r] = znxt[r];
+            vcur[r] = vn1[r];
+            zcur[r] = zn1[r];
+            vn1[r] = vn2[r];
+            zn1[r] = zn2[r];
         }
     }
 
