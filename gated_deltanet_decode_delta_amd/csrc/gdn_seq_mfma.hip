@@ -250,36 +250,38 @@ __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
     // column by column (lane column li, forward substitution with the identity
     // column as right-hand side: the entries above li come out exactly 0 and
     // x[li] exactly 1).  Lane (g, li) owns A[4g + r][li]; k.k is symmetric, so
-    // no value moves between lanes before the LDS round trip.
+    // no value moves between lanes before the LDS round trip.  A is stored
+    // transposed (a_s row s = column s of A), and the substitution is column
+    // oriented: once x[s] is final it is taken out of every later x[t], so the
+    // dependent chain is one FMA per step.
     auto solve = [&](int b3, int par) {
         if (w == kSolveWave) {
             const f32x4 bet = *reinterpret_cast<const f32x4 *>(&be_s[b3][4 * g]);
             const f32x4 mA = *reinterpret_cast<const f32x4 *>(&mt_s[par][li * kTS + 4 * g]);  // M[4g+r][li]
+            f32x4 acol;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int ai = 4 * g + r;
                 float kk = 0.f;
 #pragma unroll
                 for (int v2 = 0; v2 < kPartWaves; ++v2) kk += part_s[par][v2][0][l][r];
-                a_s[ai * kTS + li] = li < ai ? bet[r] * mA[r] * kk : 0.0f;
+                acol[r] = li < ai ? bet[r] * mA[r] * kk : 0.0f;
             }
+            *reinterpret_cast<f32x4 *>(&a_s[li * kTS + 4 * g]) = acol;   // A[4g+r][li]
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
             __builtin_amdgcn_wave_barrier();
             float x[kC];
 #pragma unroll
-            for (int t = 0; t < kC; ++t) x[t] = 0.0f;
+            for (int t = 0; t < kC; ++t) x[t] = unit[t];
 #pragma unroll
-            for (int t = 0; t < kC; ++t) {
-                float acc0 = 0.f, acc1 = 0.f;
+            for (int s2 = 0; s2 < kC - 1; ++s2) {
 #pragma unroll
-                for (int s4 = 0; s4 < (t + 3) / 4; ++s4) {
-                    const f32x4 av = *reinterpret_cast<const f32x4 *>(&a_s[t * kTS + 4 * s4]);
-                    acc0 = fmaf(av[0], x[4 * s4 + 0], acc0);
-                    acc1 = fmaf(av[1], x[4 * s4 + 1], acc1);
-                    acc0 = fmaf(av[2], x[4 * s4 + 2], acc0);
-                    acc1 = fmaf(av[3], x[4 * s4 + 3], acc1);
+                for (int t4 = (s2 + 1) / 4; t4 < kC / 4; ++t4) {
+                    const f32x4 av = *reinterpret_cast<const f32x4 *>(&a_s[s2 * kTS + 4 * t4]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (4 * t4 + e > s2) x[4 * t4 + e] = fmaf(-av[e], x[s2], x[4 * t4 + e]);
                 }
-                x[t] = unit[t] - (acc0 + acc1);
             }
             if (g == 0) {
 #pragma unroll
