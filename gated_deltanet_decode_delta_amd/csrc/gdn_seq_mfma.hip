@@ -223,8 +223,7 @@ __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
     // waves 1..3 (SIMDs 1..3) form a part each of the chunk's k.k and k.q
     // products (16-column slices 3p .. 3p + 2 of the 8); the parts are summed
     // when read.  Waves 4..7 form the range products meanwhile.
-    auto partials = [&](int b3, int par) {
-        range_products(b3, par);
+    auto tiles = [&](int b3, int par) {
         if (w >= 1 && w <= kPartWaves) {
             const int pw = w - 1;
             f32x4 KK = f32x4{0.f, 0.f, 0.f, 0.f}, KQ = KK;
@@ -244,6 +243,10 @@ __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
             part_s[par][pw][0][l] = KK;
             part_s[par][pw][1][l] = KQ;
         }
+    };
+    auto partials = [&](int b3, int par) {
+        range_products(b3, par);
+        tiles(b3, par);
     };
 
     // Wave 0: A[a][b] = beta_a M[a][b] (k_a.k_b) for b < a, then T = (I + A)^{-1}
@@ -322,8 +325,10 @@ __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
     // Per chunk c (chunk buffer b3 = c % 3, pair buffer par = c & 1), two barriers:
     //   U, W on the matrix cores (every wave alike); chunk c+2 staged
     //   -- barrier: chunk c+2 visible --
-    //   C', O, outputs, state update; prefetch of chunk c+3; chunk c+2's k.k,
-    //   k.q partials and range products; A and T of chunk c+1 (wave 0)
+    //   chunk c+2's range products (waves 4..7, first, so that the two waves of
+    //   a SIMD are not both in the dependent C' -> O chain at once); C', O,
+    //   outputs, state update; prefetch of chunk c+3; chunk c+2's k.k, k.q
+    //   partials (waves 1..3); A and T of chunk c+1 (wave 0)
     //   -- barrier: chunk c+2 prepared, T(c+1) visible, every read of chunk c done --
     float *outp = static_cast<float *>(a.out);
     for (int t0 = 0, b3 = 0, par = 0; t0 < T; t0 += kC, b3 = b3 == kBufs - 1 ? 0 : b3 + 1, par ^= 1) {
@@ -364,6 +369,7 @@ __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
             take(vn2, zn2);
         }
         __syncthreads();   // chunk c+2 staged
+        if (t0 + 2 * kC < T) range_products(b3n2, par);   // waves 4..7, ahead of their state work
 
         const f32x4 bet = *reinterpret_cast<const f32x4 *>(&be_s[b3][4 * g]);
         const f32x4 Ta = *reinterpret_cast<const f32x4 *>(&t_s[par][li * kTS + 4 * g]);
@@ -449,7 +455,7 @@ __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
         // chunk c+3's loads go out after this chunk's output stores: the wait for
         // them (at the next staging) then never waits on a store issued later
         if (t0 + 3 * kC < T) prefetch(t0 + 3 * kC);
-        if (t0 + 2 * kC < T) partials(b3n2, par);   // chunk c+2 uses pair buffer par too
+        if (t0 + 2 * kC < T) tiles(b3n2, par);   // chunk c+2 uses pair buffer par too
         if (t0 + kC < T) solve(b3n1, par ^ 1);
         __syncthreads();   // chunk c+2 prepared; T(c+1) visible; every read of chunk c done
 #pragma unroll
