@@ -364,8 +364,8 @@ def test_every_head_dim_all_entry_points(g, D, NV, NK):
 @pytest.mark.parametrize("D", [4, 8, 16, 32, 64, 128, 256])
 def test_wide_launch_every_head_dim(g, D):
     """Launches of 256 or more workgroups use the wide single-token tile (16
-    values per lane for fp32, 32 for binary16); smaller ones the 256-thread
-    tile.  Every decode mode at every D on a wide launch (B=32, NV=8, NK=4)."""
+    values per lane for fp32, 32 for binary16); smaller ones hold 32 values per
+    lane.  Every decode mode at every D on a wide launch (B=32, NV=8, NK=4)."""
     import torch
     B, NK, NV = 32, 4, 8
     c = inputs.make_case(1100 + D, B=B, NK=NK, NV=NV, D=D)
