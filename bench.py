@@ -343,6 +343,18 @@ def run_real_head(g, tokens: int):
     return res
 
 
+def cpu_model() -> str:
+    """The host CPU's model name, as /proc/cpuinfo gives it (empty if unknown)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
 def cpu_baseline(seconds: float):
     """The oracle on a bounded sample of the main workload: whole B=64 calls,
     (sequence, head) pairs fanned out over the host's threads (capped at 16)."""
@@ -370,7 +382,7 @@ def cpu_baseline(seconds: float):
                   gn=c.gn, eps=c.eps)
     el1 = time.perf_counter() - t1
     return {"value": round(state_bytes / el / 1e9, 3), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{calls} full B=64 gdn_decode_norm calls (3072 heads each) in {el:.1f} s "
                       f"on {threads} host threads; state GB/s by the same formula",
             "tokens_per_s_batch": round(B * calls / el, 1),
@@ -546,7 +558,7 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
         sys.exit(2)
 

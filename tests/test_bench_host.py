@@ -1,0 +1,75 @@
+"""Host-side logic of bench.py (no GPU): the algorithmic byte counts the
+roofline fractions are quoted with, and the counter-traffic record (scaling by
+the device copy, and withheld once the kernel sources change)."""
+import json
+
+import pytest
+
+import bench
+
+
+def test_head_bytes_match_the_stated_per_launch_figures():
+    # B=64 fp32 fused-norm decode: 64 KiB tile read + written, q and k of the
+    # key head shared by 3 value heads, v, alpha, beta, z and the fp32 output
+    per_head = 2 * 128 * 128 * 4 + 2 * 128 * 4 / 3 + 128 * 4 + 8 + 128 * 4 + 128 * 4
+    assert bench.head_bytes(128, 48, 16, 4, 4, True) == pytest.approx(per_head)
+    assert round(64 * 48 * bench.head_bytes(128, 48, 16, 4, 4, True)) == 408_444_928
+    # B=256 binary16 state with a bf16 output
+    assert round(256 * 48 * bench.head_bytes(128, 48, 16, 2, 2, True)) == 825_327_616
+    # raw output: no z
+    assert bench.head_bytes(128, 48, 16, 4, 4, False) == pytest.approx(per_head - 128 * 4)
+
+
+def _counter_csv(path, counter, rows):
+    with open(path, "w") as f:
+        f.write("Kernel_Name,Counter_Name,Counter_Value\n")
+        for name, value in rows:
+            f.write(f'"{name}",{counter},{value}\n')
+
+
+def test_pmc_record_scaling_and_hash_gate(tmp_path, monkeypatch):
+    kernel = "void gdn::decode_kernel<128, float, 1, 16>(gdn::StepArgs)"
+    copy = "__amd_rocclr_copyBuffer"
+    fetch, write = tmp_path / "fetch.csv", tmp_path / "write.csv"
+    # the 1 GiB copy reads 512 Ki KiB of FETCH_SIZE (factor 2) and writes
+    # 1 Mi KiB of WRITE_SIZE (factor 1); a smaller copy must not be taken
+    _counter_csv(fetch, "FETCH_SIZE", [(copy, 1000.0), (copy, 524288.0), (kernel, 100000.0),
+                                       (kernel, 100002.0)])
+    _counter_csv(write, "WRITE_SIZE", [(copy, 2000.0), (copy, 1048576.0), (kernel, 200000.0),
+                                       (kernel, 200000.0)])
+    out = tmp_path / "pmc.json"
+    monkeypatch.setattr(bench, "PMC_FILE", str(out))
+    bench.pmc_summarize(str(fetch), str(write))
+    rec = json.loads(out.read_text())
+    assert rec["calibration"]["fetch_factor"] == pytest.approx(2.0)
+    assert rec["calibration"]["write_factor"] == pytest.approx(1.0)
+    assert rec["fetch_bytes_per_launch"] == int(100001.0 * 1024 * 2)
+    assert rec["write_bytes_per_launch"] == int(200000.0 * 1024)
+    assert rec["bytes_per_launch"] == rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+    assert rec["kernel_hash"] == bench.kernel_hash()
+    assert bench.pmc_traffic(408_444_928) == rec["bytes_per_launch"]
+    # a record taken on other kernel sources is not reported
+    rec["kernel_hash"] = "0" * 16
+    out.write_text(json.dumps(rec))
+    assert bench.pmc_traffic(408_444_928) is None
+
+
+def test_committed_record_names_the_timed_kernel():
+    with open(bench.PMC_FILE) as f:
+        rec = json.load(f)
+    assert rec["kernel"] == "void gdn::decode_kernel<128, float, 1, 16>(gdn::StepArgs)"
+    assert rec["algorithmic_bytes_per_launch"] == 408_444_928
+    assert rec["kernel_sources"] == list(bench.KERNEL_SOURCES)
+
+
+def test_cpu_model_is_a_string():
+    assert isinstance(bench.cpu_model(), str)
+
+
+def test_more_than_one_gpu_is_refused_before_any_gpu_work():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and "--gpus 2" in r.stderr
