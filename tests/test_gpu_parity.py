@@ -8,6 +8,7 @@ binary16 state; bf16 outputs may also differ by half a bf16 ulp.  Full-size
 workloads are checked on every head when the oracle is fast enough, otherwise
 on sampled heads that the oracle computes one by one.
 """
+import os
 import sys
 
 import numpy as np
@@ -509,6 +510,29 @@ def test_converters_bitwise(g):
     assert np.array_equal(back[fin].view(np.uint32), ref[fin].view(np.uint32))
     assert np.isnan(back[~fin]).all()
     del torch
+
+
+def test_f32_to_f16_every_binary32_pattern(g):
+    """The fp32 -> binary16 converter on all 2^32 binary32 bit patterns, in 16
+    chunks, bitwise against the oracle's RNE (NaNs: any quiet binary16 NaN)."""
+    from concurrent.futures import ThreadPoolExecutor
+    import torch
+    n = 1 << 28
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    src = torch.empty(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty(n, dtype=torch.float16, device="cuda:0")
+    for chunk in range(16):
+        x = np.arange(chunk * n, (chunk + 1) * n, dtype=np.uint32).view(np.float32)
+        say("f32 -> f16 patterns", chunk, "of 16")
+        src.copy_(torch.from_numpy(x))
+        g.gdn_state_f32_to_f16(src, dst)
+        got = host(dst)
+        parts = np.array_split(np.arange(n), threads)
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            want = np.concatenate(list(ex.map(lambda ix: orc.f32_to_f16_bits(x[ix[0]:ix[-1] + 1]), parts)))
+        nan = np.isnan(x)
+        assert np.array_equal(got[~nan], want[~nan]), chunk
+        assert ((got[nan] & 0x7C00) == 0x7C00).all() and (got[nan] & 0x03FF).all(), chunk
 
 
 def test_f16_state_keeps_subnormals(g):
