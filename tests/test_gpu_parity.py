@@ -464,6 +464,44 @@ def test_deterministic_bitwise(g):
     assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
 
 
+@pytest.mark.parametrize("kind", ["decode", "f16", "seq128", "seq64"])
+def test_batch_permutation_permutes_results_bitwise(g, kind):
+    """Sequences are independent: running a permuted batch gives the permuted
+    outputs and states bit for bit (a wide launch for every kernel family)."""
+    import torch
+    D = 64 if kind == "seq64" else 128
+    T = 20 if kind.startswith("seq") else 1
+    B, NK, NV = (8, 4, 8) if kind.startswith("seq") else (40, 4, 8)
+    c = inputs.make_case(1900 + D + T, B=B, NK=NK, NV=NV, D=D, T=T)
+    perm = np.random.Generator(np.random.PCG64(19)).permutation(B)
+    rows = (perm[:, None] * T + np.arange(T)[None, :]).reshape(-1)
+    say("batch permutation", kind)
+
+    def run(order, row_order):
+        d = {n: dev(np.ascontiguousarray(getattr(c, n)[row_order]))
+             for n in ("q", "k", "v", "z", "alpha", "beta")}
+        st32 = dev(np.ascontiguousarray(c.state[order]))
+        if kind == "decode":
+            y = g.gdn_decode_norm(st32, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["z"],
+                                  dev(c.gn), c.eps, num_k_heads=NK, num_v_heads=NV)
+            return host(y), host(st32).view(np.uint32)
+        if kind == "f16":
+            st16 = g.gdn_state_f32_to_f16(st32)
+            y = g.gdn_decode_f16state(st16, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["z"],
+                                      dev(c.gn), c.eps, out_dtype=torch.bfloat16, num_k_heads=NK,
+                                      num_v_heads=NV)
+            return host(y), host(st16)
+        o = g.gdn_recurrence_seq(st32, d["q"], d["k"], d["v"], d["alpha"], d["beta"], seq_len=T,
+                                 num_k_heads=NK, num_v_heads=NV, head_dim=D)
+        return host(o), host(st32).view(np.uint32)
+
+    base = np.arange(B)
+    y0, s0 = run(base, np.arange(B * T))
+    y1, s1 = run(perm, rows)
+    assert np.array_equal(y1, y0[rows])
+    assert np.array_equal(s1, s0[perm])
+
+
 def test_empty_batch_and_length_are_noops(g):
     import torch
     c = inputs.make_case(63, B=2, NK=2, NV=4, D=16, T=1)
