@@ -329,7 +329,8 @@ gdn_status gdn_decode_fused(float *state, int64_t state_seq_stride, float *conv_
         k_dim <= 0 || v_dim <= 0 || taps < 1 || taps > gdn::kMaxTaps)
         return GDN_ERR_SHAPE;
     if (k_dim != v_dim || !supported_dim(k_dim)) return GDN_ERR_UNSUPPORTED;
-    if ((int64_t)batch * num_k_heads > INT32_MAX) return GDN_ERR_SHAPE;
+    // the two-buffer launch has batch * num_v_heads workgroups (the larger grid)
+    if ((int64_t)batch * num_v_heads > INT32_MAX) return GDN_ERR_SHAPE;
     if (!isfinite(l2_eps) || l2_eps < 0.0f) return GDN_ERR_ARG;
     if (norm && (!isfinite(eps) || eps < 0.0f)) return GDN_ERR_ARG;
     const int32_t D = k_dim;

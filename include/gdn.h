@@ -70,7 +70,8 @@ extern "C" {
 typedef enum gdn_status {
     GDN_OK = 0,
     GDN_ERR_NULL = 1,        /* a required pointer is NULL                                   */
-    GDN_ERR_SHAPE = 2,       /* negative batch/seq_len, non-positive heads, NV % NK != 0      */
+    GDN_ERR_SHAPE = 2,       /* negative batch/seq_len, non-positive heads, NV % NK != 0,
+                                batch * num_v_heads above INT32_MAX (one launch's grid)       */
     GDN_ERR_STRIDE = 3,      /* stride/pitch too small for its row, or misaligned pointer     */
     GDN_ERR_UNSUPPORTED = 4, /* k_dim != v_dim, or not a power of two in [4, 256]             */
     GDN_ERR_ALIAS = 5,       /* state/out overlaps an input or each other; converter in-place */

@@ -243,6 +243,8 @@ def test_fused_validation(lib):
     assert fused(lib, rout=p["inter"] + (1 << 20) + 4) == 3  # misaligned new ring
     assert fused(lib, nk=1, nv=64, dk=256, dv=256, rout=p["inter"] + (1 << 20)) != 4
     assert fused(lib, B=0) == 0
+    # 2^26 sequences x 64 value heads is past a 32-bit grid, though x 1 key head is not
+    assert fused(lib, B=1 << 26, nk=1, nv=64, rout=p["inter"] + (1 << 20)) == 2
 
 
 def test_converter_validation(lib):
