@@ -78,9 +78,9 @@ def _lib():
                                       vp, f32, vp, i64, i32, i32, i32, i32, i32, i32, vp]
     lib.gdn_state_f32_to_f16.argtypes = [vp, vp, i64, vp]
     lib.gdn_state_f16_to_f32.argtypes = [vp, vp, i64, vp]
-    for name in ("gdn_decode", "gdn_decode_norm", "gdn_decode_norm_q", "gdn_decode_f16state",
-                 "gdn_recurrence_seq", "gdn_decode_verify", "gdn_decode_fused", "gdn_state_f32_to_f16", "gdn_state_f16_to_f32"):
-        getattr(lib, name).restype = ctypes.c_int
+    for name in EXPORTS:
+        if name not in ("gdn_status_string", "gdn_last_hip_error"):
+            getattr(lib, name).restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_last_hip_error.argtypes = []
