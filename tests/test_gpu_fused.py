@@ -86,6 +86,23 @@ def test_fused_against_oracle(g, D, NV, NK, taps, norm, split):
     assert np.isnan(got[:, NV * D * D:]).all()
 
 
+@pytest.mark.parametrize("taps", [2, 3, 5, 6, 7])
+@pytest.mark.parametrize("split", [False, True])
+def test_fused_every_ring_depth(g, taps, split):
+    """The ring depths not covered above, on both sides of the short-ring variant
+    (taps <= 4): D = 128, the decode's 3:1 pairing, fused norm, a wide enough
+    launch (B = 64) that the two-buffer kernel takes its 256-workgroup shape."""
+    B, NK, NV, D = 64, 2, 6, 128
+    c = inputs.make_frontend_case(940 + taps, B=B, NK=NK, NV=NV, D=D, taps=taps,
+                                  ring_pitch=taps * (2 * NK + NV) * D + 4)
+    say("fused ring depth", taps, "split" if split else "in place")
+    d, o = _gpu(g, c, True, split)
+    st, ring, y = _oracle(c, True)
+    assert np.array_equal(_new_ring(d, c), ring[:, :c.taps * c.C])
+    assert out_err(host(o), y, NV, D) < TOL_STEP
+    assert tile_err(host(d["state"]), st, NV, D) < TOL_STEP
+
+
 @pytest.mark.parametrize("split", [False, True])
 def test_fused_real_shape_full_batch(g, split):
     """The decode workload's shapes (B=64, 48 value heads over 16 key heads,
