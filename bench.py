@@ -102,6 +102,9 @@ def run_main(g, steps: int, warmup: int, pools: int):
 
     ms = _timed(step, steps, warmup)
     ms_hot = _timed(lambda i: step(0), steps, warmup)
+    # five further trials of 200 rotated calls each (median and minimum reported
+    # beside the main figure, which stays the one timed region above)
+    trials = sorted(_timed(step, 200, 5) for _ in range(5))
     state_bytes = 2.0 * B * NV * D * D * 4
     algo_bytes = B * NV * head_bytes(D, NV, NK, 4, 4, True)
     torch.cuda.synchronize()
@@ -109,6 +112,7 @@ def run_main(g, steps: int, warmup: int, pools: int):
     del states, sets, outs
     torch.cuda.empty_cache()
     return dict(B=B, NV=NV, NK=NK, D=D, pitch=pitch, pools=pools, ms=ms, ms_hot=ms_hot,
+                trials=trials,
                 state_bytes=state_bytes, algo_bytes=algo_bytes, nonfinite=bad)
 
 
@@ -531,7 +535,8 @@ def pmc_summarize(fetch_csv: str, write_csv: str):
     with open(PMC_FILE, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
-    print(json.dumps({"bytes_per_launch": rec["bytes_per_launch"], "algorithmic": rec["algorithmic_bytes_per_launch"]}))
+    print(json.dumps({"bytes_per_launch": rec["bytes_per_launch"],
+                      "algorithmic": rec["algorithmic_bytes_per_launch"]}))
 
 
 def main():
@@ -584,7 +589,10 @@ def main():
     extra = {"cache_resident_single_pool": {
         "ms_per_call": round(m["ms_hot"], 5),
         "state_GBps": round(m["state_bytes"] / m["ms_hot"] / 1e6, 1),
-        "note": "same pool every call: the 201 MB state can stay in the 256 MB Infinity Cache"}}
+        "note": "same pool every call: the 201 MB state can stay in the 256 MB Infinity Cache"},
+        "trials_5x200": {"median_ms": round(m["trials"][2], 5), "min_ms": round(m["trials"][0], 5),
+                         "median_hbm_frac_algorithmic": round(
+                             m["algo_bytes"] / m["trials"][2] / 1e6 / HBM_PEAK_GBS, 4)}}
     wanted = [] if args.no_extra else [w for w in args.extras.split(",") if w]
     runners = {"fp16_state": lambda: run_fp16(g, 100), "sequence": lambda: run_seq(g, 5),
                "verify": lambda: run_verify(g, 100), "norm_q": lambda: run_norm_q(g, 200),
