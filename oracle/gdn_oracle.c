@@ -42,7 +42,9 @@
  * algebraically equal o = (alpha S q + coef (k.q)) / sqrt(Dk); keeping the two
  * forms apart is what makes a formula slip on either side show up.
  *
- * Layout readings (the pages differ; see the reading list in the docs):
+ * Layout readings (logicaffeine's `gdn_step` indexes the memory value-row major,
+ * while metrale's comments describe the transposed [k_dim, v_dim] order; the
+ * sizes agree because Dk = Dv, and this follows the first page's arithmetic):
  *   state slot of (b, h) at  b*pitch + h*Dv*Dk,  row i = value index, column j =
  *   key index (key index contiguous);  token row r = b*T + t;  q/k element
  *   r*qk_stride + g*Dk + j;  v/z/out element r*stride + h*Dv + i;  alpha/beta
