@@ -35,7 +35,8 @@ STATUS_NAMES = {
     8: "GDN_ERR_ARG",
 }
 EXPORTS = ("gdn_decode", "gdn_decode_norm", "gdn_decode_norm_q", "gdn_decode_f16state",
-           "gdn_recurrence_seq", "gdn_decode_verify", "gdn_decode_fused", "gdn_state_f32_to_f16",
+           "gdn_recurrence_seq", "gdn_recurrence_seq_ws", "gdn_seq_workspace_bytes",
+           "gdn_decode_verify", "gdn_decode_fused", "gdn_state_f32_to_f16",
            "gdn_state_f16_to_f32", "gdn_status_string", "gdn_last_hip_error")
 VERIFY_MAX_TOKENS = 8
 
@@ -70,6 +71,9 @@ def _lib():
     lib.gdn_decode_f16state.argtypes = norm_sig
     lib.gdn_recurrence_seq.argtypes = [vp, i64, vp, vp, i64, vp, i64, vp, vp, i64, vp, i64, vp,
                                        f32, vp, i64, i32, i32, i32, i32, i32, i32, vp]
+    lib.gdn_recurrence_seq_ws.argtypes = [vp, i64, vp, vp, i64, vp, i64, vp, vp, i64, vp, i64, vp,
+                                          f32, vp, i64, i32, i32, i32, i32, i32, i32, vp, i64, vp]
+    lib.gdn_seq_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.gdn_decode_norm_q.argtypes = [vp, i64, vp, vp, i64, vp, i64, vp, vp, i64, vp, i64, vp, f32,
                                       vp, i64, vp, i64, vp, i64, i32, i32, i32, i32, i32, vp]
     lib.gdn_decode_fused.argtypes = [vp, i64, vp, i64, vp, vp, i64, vp, i32, vp, vp, i64, vp, vp, f32,
@@ -79,8 +83,9 @@ def _lib():
     lib.gdn_state_f32_to_f16.argtypes = [vp, vp, i64, vp]
     lib.gdn_state_f16_to_f32.argtypes = [vp, vp, i64, vp]
     for name in EXPORTS:
-        if name not in ("gdn_status_string", "gdn_last_hip_error"):
+        if name not in ("gdn_status_string", "gdn_last_hip_error", "gdn_seq_workspace_bytes"):
             getattr(lib, name).restype = ctypes.c_int
+    lib.gdn_seq_workspace_bytes.restype = i64
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_last_hip_error.argtypes = []
@@ -285,10 +290,8 @@ def gdn_decode_f16state(state, q, k, v, alpha, beta, z=None, norm_weight=None, e
                       stream, raw_ok=True)
 
 
-def gdn_recurrence_seq(state, q, k, v, alpha, beta, z=None, norm_weight=None, eps: float = 1e-6,
-                       out=None, *, seq_len: int, num_k_heads: int, num_v_heads: int,
-                       head_dim: Optional[int] = None, stream=None):
-    """``seq_len`` tokens per sequence with the state on chip; returns o (or y) rows."""
+def _seq_args(state, q, k, v, alpha, beta, z, norm_weight, out, seq_len, num_k_heads, num_v_heads,
+              head_dim):
     torch = _torch()
     B = state.shape[0]
     T = int(seq_len)
@@ -314,9 +317,49 @@ def gdn_recurrence_seq(state, q, k, v, alpha, beta, z=None, norm_weight=None, ep
     else:
         zp, zs, gp = None, 0, None
     op, os_, _ = _rows(out, rows, NV * D, "out", torch.float32)
-    _check(_lib().gdn_recurrence_seq(sp, pitch, qp, kp, qs, vp_, vs, ap, bp, abs_, zp, zs, gp,
-                                     float(eps), op, os_, B, T, NK, NV, D, D,
-                                     _stream(state, stream)), "gdn_recurrence_seq")
+    head = (sp, pitch, qp, kp, qs, vp_, vs, ap, bp, abs_, zp, zs, gp)
+    tail = (op, os_, B, T, NK, NV, D, D)
+    return out, head, tail
+
+
+def gdn_recurrence_seq(state, q, k, v, alpha, beta, z=None, norm_weight=None, eps: float = 1e-6,
+                       out=None, *, seq_len: int, num_k_heads: int, num_v_heads: int,
+                       head_dim: Optional[int] = None, stream=None):
+    """``seq_len`` tokens per sequence with the state on chip; returns o (or y) rows."""
+    out, head, tail = _seq_args(state, q, k, v, alpha, beta, z, norm_weight, out, seq_len,
+                                num_k_heads, num_v_heads, head_dim)
+    _check(_lib().gdn_recurrence_seq(*head, float(eps), *tail, _stream(state, stream)),
+           "gdn_recurrence_seq")
+    return out
+
+
+def gdn_seq_workspace_bytes(batch: int, seq_len: int, num_v_heads: int, head_dim: int) -> int:
+    """Bytes of workspace ``gdn_recurrence_seq_ws`` uses for this shape (0: none)."""
+    n = int(_lib().gdn_seq_workspace_bytes(int(batch), int(seq_len), int(num_v_heads),
+                                           int(head_dim), int(head_dim)))
+    if n < 0:
+        raise ValueError("invalid sequence shape")
+    return n
+
+
+def gdn_recurrence_seq_ws(state, q, k, v, alpha, beta, z=None, norm_weight=None,
+                          eps: float = 1e-6, out=None, workspace=None, *, seq_len: int,
+                          num_k_heads: int, num_v_heads: int, head_dim: Optional[int] = None,
+                          stream=None):
+    """``gdn_recurrence_seq`` with a device workspace (a uint8 tensor of at least
+    ``gdn_seq_workspace_bytes`` bytes; allocated here when not given)."""
+    torch = _torch()
+    out, head, tail = _seq_args(state, q, k, v, alpha, beta, z, norm_weight, out, seq_len,
+                                num_k_heads, num_v_heads, head_dim)
+    B, T, NV, D = tail[2], tail[3], tail[5], tail[6]
+    need = gdn_seq_workspace_bytes(B, T, NV, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=state.device)
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(_lib().gdn_recurrence_seq_ws(*head, float(eps), *tail, workspace.data_ptr(), nbytes,
+                                        _stream(state, stream)), "gdn_recurrence_seq_ws")
     return out
 
 

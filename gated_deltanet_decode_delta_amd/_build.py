@@ -27,13 +27,19 @@ FLAGS = [
 ]
 
 
+# Per-source extra flags.  The split sequence kernel keeps its matrix-core
+# accumulators in ordinary VGPRs: left to itself the compiler puts them in
+# AGPRs and copies every one back for the vector-ALU work on it.
+EXTRA = {"gdn_seq_split.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(line for line in res.stderr.splitlines()
                      if "packed-fp32-ops" not in line and line.strip())

@@ -287,6 +287,51 @@ gdn_status gdn_recurrence_seq(float *state, int64_t state_seq_stride, const floa
                                   norm ? gdn::kOutNormF32 : gdn::kOutRawF32, (hipStream_t)stream));
 }
 
+int64_t gdn_seq_workspace_bytes(int32_t batch, int32_t seq_len, int32_t num_v_heads,
+                                int32_t k_dim, int32_t v_dim) {
+    if (batch < 0 || seq_len < 0 || num_v_heads < 0) return -1;
+    if (k_dim != 128 || v_dim != 128) return 0;
+    const __int128 chunks = ((__int128)seq_len + 15) / 16;
+    const __int128 bytes = (__int128)batch * num_v_heads * chunks * gdn::kSeqRec * 4;
+    if (bytes > kMaxBytes) return -1;
+    return (int64_t)bytes;
+}
+
+gdn_status gdn_recurrence_seq_ws(float *state, int64_t state_seq_stride, const float *q,
+                                 const float *k, int64_t qk_stride, const float *v,
+                                 int64_t v_stride, const float *alpha, const float *beta,
+                                 int64_t ab_stride, const float *z, int64_t z_stride,
+                                 const float *norm_weight, float eps, float *out,
+                                 int64_t out_stride, int32_t batch, int32_t seq_len,
+                                 int32_t num_k_heads, int32_t num_v_heads, int32_t k_dim,
+                                 int32_t v_dim, void *workspace, int64_t workspace_bytes,
+                                 void *stream) {
+    const bool norm = z != nullptr;
+    Call c{state, state_seq_stride, 4, q, k, qk_stride, v, v_stride, alpha, beta, ab_stride,
+           z, z_stride, norm_weight, eps, norm, out, 4, out_stride,
+           batch, seq_len, num_k_heads, num_v_heads, k_dim, v_dim};
+    bool empty;
+    Spans sp;
+    gdn_status s = validate(c, &empty, &sp);
+    if (s != GDN_OK || empty) return s;
+    gdn::StepArgs a = to_args(c, state, out);
+    if (norm || k_dim != 128)
+        return finish(gdn::launch_seq(a, k_dim, norm ? gdn::kOutNormF32 : gdn::kOutRawF32,
+                                      (hipStream_t)stream));
+    const int64_t need = gdn_seq_workspace_bytes(batch, seq_len, num_v_heads, k_dim, v_dim);
+    if (need < 0) return GDN_ERR_SHAPE;
+    // one pre-pass workgroup per (sequence, key head, chunk), four per value head
+    if ((int64_t)batch * num_k_heads * ((seq_len + 15) / 16) > INT32_MAX ||
+        (int64_t)batch * num_v_heads * 4 > INT32_MAX)
+        return GDN_ERR_SHAPE;
+    if (!workspace) return GDN_ERR_NULL;
+    if (workspace_bytes < need) return GDN_ERR_ARG;
+    Span ws;
+    s = check_extra_out(sp, workspace, 1, need / 4, need / 4, 4, 16, &ws);
+    if (s != GDN_OK) return s;
+    return finish(gdn::launch_seq_split(a, static_cast<float *>(workspace), (hipStream_t)stream));
+}
+
 gdn_status gdn_decode_verify(float *state, int64_t state_seq_stride, float *inter_state,
                              int64_t inter_pitch, const float *q, const float *k, int64_t qk_stride,
                              const float *v, int64_t v_stride, const float *alpha, const float *beta,

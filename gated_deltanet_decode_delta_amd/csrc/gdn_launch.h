@@ -68,6 +68,12 @@ hipError_t launch_fused(const StepArgs &a, const FrontArgs &f, float *ring_out, 
                         hipStream_t stream);
 size_t fused_lds_bytes(int dim, int heads_per_key_head);
 hipError_t launch_seq_mfma(const StepArgs &a, OutMode mode, hipStream_t stream);   // dim 128
+// Floats of one workspace record of the split sequence path: one per (sequence,
+// value head, 16-token chunk) -- T and G (16x16 each, row-major), beta, P and D.
+constexpr int kSeqRec = 576;
+// dim 128, raw output: chunk pre-pass into ws, then the state pass (four
+// workgroups per head)
+hipError_t launch_seq_split(const StepArgs &a, float *ws, hipStream_t stream);
 hipError_t launch_f32_to_f16(const float *src, uint16_t *dst, int64_t n, hipStream_t stream);
 hipError_t launch_f16_to_f32(const uint16_t *src, float *dst, int64_t n, hipStream_t stream);
 

@@ -1,0 +1,399 @@
+// gdn_seq_split.hip -- the T-token recurrence at D = 128, raw output, with the
+// state-independent chunk quantities formed once ahead and each head split over
+// four workgroups.
+//
+// Same chunked algebra as gdn_seq_mfma.hip (16 tokens per chunk; metrale
+// "layers/ops/ssm_gdn_a.rs" `gdn_prefill_regresident` for the operation, the
+// update of logicaffeine "codegen_cuda/gdn.rs" `gdn_step`): with M[t][s] =
+// alpha_{s+1} ... alpha_t, P_t = alpha_0 ... alpha_t and S0 the state at the
+// chunk start,
+//     C' = T R,  R = beta (V - P S0 K^T),  T = (I + A)^{-1},
+//          A[t][s] = beta_t M[t][s] (k_s.k_t)  (s < t)
+//     O  = P S0 Q^T + C' G^T,  G[t][s] = M[t][s] (k_s.q_t)  (s <= t)
+//     S_end = P_15 S0 + C' diag(M[15][.]) K.
+// T, G, beta, P and D = M[15][.] depend on the inputs only.  A pre-pass
+// (`prep_kernel`) forms them for every (sequence, value head, chunk) into a
+// workspace: the k.k and k.q tiles once per key head instead of once per value
+// head, and the triangular inverse by forward substitution off the state
+// kernel's SIMDs.
+//
+// The state pass (`split_kernel`): one workgroup of four waves per quarter of a
+// head (32 state rows).  Wave (strip, half) owns rows 16 strip .. +15 of the
+// quarter and key columns 64 half .. +63: four 16x16 accumulator tiles.  The
+// two halves of a strip form partial U = S0 K^T and W = S0 Q^T over their
+// columns and exchange them through LDS, then both run the chain for their
+// strip and update their own columns.  192 heads make 768 workgroups, three per
+// CU and three waves per SIMD on all 256 CUs, each wave issuing 56 matrix-core
+// products per chunk (a workgroup per head puts two 104-product waves on each
+// SIMD of 192 CUs).  Waves of different workgroups share a SIMD, so one
+// workgroup's barrier and chain latency are covered by the others' products.
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kD = 128;
+constexpr int kC = 16;            // tokens per chunk
+constexpr int kKS = kD + 4;       // LDS row stride (floats) of k / q
+constexpr int kTS = kC + 1;       // LDS row stride of 16x16 matrices in the pre-pass
+
+__device__ __forceinline__ f32x4 mfma(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// The value of the lane N places higher in the same 16-lane DPP row, or 1 past
+// the end of the row.
+template <int N>
+__device__ __forceinline__ float dpp_from_above(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(x), 0x100 + N,
+                                                      0xF, 0xF, false));
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Pre-pass: one wave per (sequence b, key head kh, chunk c).  Tokens past T
+// get alpha 1, beta 0 and zero k, q, so they change nothing.
+__global__ void __launch_bounds__(64) prep_kernel(StepArgs a, float *ws, int nc) {
+    __shared__ __align__(16) float k_s[kC * kKS], q_s[kC * kKS];
+    __shared__ float m_s[kC * kTS];    // M[t][s]
+    __shared__ float a_s[kC * kTS];    // a_s[s][t] = A[t][s]
+    __shared__ float t_s[kC * kTS];    // T[t][s]
+    __shared__ float al_s[kC + 1], be_s[kC];
+
+    const int l = threadIdx.x, g = l >> 4, li = l & 15;
+    const int item = blockIdx.x;
+    const int c = item % nc;
+    const int bk = item / nc;
+    const int kh = bk % a.nk;
+    const int b = bk / a.nk;
+    const int T = a.seq_len;
+    const int t0 = c * kC;
+    const int64_t row_base = (int64_t)b * T;
+
+#pragma unroll
+    for (int u = 0; u < kC * kD / 4 / 64; ++u) {
+        const int f = l + 64 * u;
+        const int t = f >> 5, col = (f & 31) * 4;
+        const bool ok = t0 + t < T;
+        const int64_t off = (row_base + (ok ? t0 + t : T - 1)) * a.qk_stride + (int64_t)kh * kD + col;
+        const float4 kx = *reinterpret_cast<const float4 *>(a.k + off);
+        const float4 qx = *reinterpret_cast<const float4 *>(a.q + off);
+        *reinterpret_cast<float4 *>(&k_s[t * kKS + col]) =
+            make_float4(ok ? kx.x : 0.f, ok ? kx.y : 0.f, ok ? kx.z : 0.f, ok ? kx.w : 0.f);
+        *reinterpret_cast<float4 *>(&q_s[t * kKS + col]) =
+            make_float4(ok ? qx.x : 0.f, ok ? qx.y : 0.f, ok ? qx.z : 0.f, ok ? qx.w : 0.f);
+    }
+    __syncthreads();
+    // lane (g, li), register r: KK[r] = k_{4g+r}.k_{li}, KQ[r] = k_{4g+r}.q_{li}
+    f32x4 K0 = f32x4{0.f, 0.f, 0.f, 0.f}, K1 = K0, Q0 = K0, Q1 = K0;
+#pragma unroll
+    for (int m = 0; m < kD / 16; ++m) {
+        const f32x4 ka = *reinterpret_cast<const f32x4 *>(&k_s[li * kKS + 16 * m + 4 * g]);
+        const f32x4 qa = *reinterpret_cast<const f32x4 *>(&q_s[li * kKS + 16 * m + 4 * g]);
+        K0 = mfma(ka[0], ka[0], K0);
+        Q0 = mfma(ka[0], qa[0], Q0);
+        K1 = mfma(ka[1], ka[1], K1);
+        Q1 = mfma(ka[1], qa[1], Q1);
+        K0 = mfma(ka[2], ka[2], K0);
+        Q0 = mfma(ka[2], qa[2], Q0);
+        K1 = mfma(ka[3], ka[3], K1);
+        Q1 = mfma(ka[3], qa[3], Q1);
+    }
+    const f32x4 KK = K0 + K1, KQ = Q0 + Q1;
+
+    const int rep = a.nv / a.nk;
+    for (int m = 0; m < rep; ++m) {
+        const int h = kh + m * a.nk;   // tiled pairing: value heads g, g + NK, ...
+        {
+            const bool ok = t0 + li < T;
+            const int64_t rr = row_base + (ok ? t0 + li : T - 1);
+            const float ax = a.alpha[rr * a.ab_stride + h];
+            const float bx = a.beta[rr * a.ab_stride + h];
+            __syncthreads();   // the previous head's reads of al_s .. t_s are done
+            if (g == 0) {
+                al_s[li] = ok ? ax : 1.0f;
+                be_s[li] = ok ? bx : 0.0f;
+            }
+            __syncthreads();
+        }
+        // M[4g + r][li] by suffix products along the DPP row (no division)
+        f32x4 Mv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 4 * g + r;
+            float x = li < t ? al_s[li + 1] : 1.0f;
+            x *= dpp_from_above<1>(x);
+            x *= dpp_from_above<2>(x);
+            x *= dpp_from_above<4>(x);
+            x *= dpp_from_above<8>(x);
+            Mv[r] = t >= li ? x : 0.0f;
+            m_s[t * kTS + li] = Mv[r];
+            a_s[li * kTS + t] = li < t ? be_s[t] * Mv[r] * KK[r] : 0.0f;
+        }
+        __syncthreads();
+        // T = (I + A)^{-1}, column li per lane (column-oriented forward substitution)
+        float x[kC];
+#pragma unroll
+        for (int t = 0; t < kC; ++t) x[t] = t == li ? 1.0f : 0.0f;
+#pragma unroll
+        for (int s2 = 0; s2 < kC - 1; ++s2)
+#pragma unroll
+            for (int t = s2 + 1; t < kC; ++t) x[t] = fmaf(-a_s[s2 * kTS + t], x[s2], x[t]);
+        if (g == 0) {
+#pragma unroll
+            for (int t = 0; t < kC; ++t) t_s[t * kTS + li] = x[t];
+        }
+        __syncthreads();
+        // workspace record: T row-major, G row-major, beta, P, D
+        float *rec = ws + (((int64_t)b * a.nv + h) * nc + c) * kSeqRec;
+        f32x4 Tr, Gr;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            Tr[r] = t_s[li * kTS + 4 * g + r];
+            Gr[r] = m_s[li * kTS + 4 * g + r] * KQ[r];   // G[li][4g+r] = M[li][4g+r] k_{4g+r}.q_{li}
+        }
+        *reinterpret_cast<f32x4 *>(rec + li * kC + 4 * g) = Tr;
+        *reinterpret_cast<f32x4 *>(rec + 256 + li * kC + 4 * g) = Gr;
+        if (g == 0) rec[512 + li] = be_s[li];
+        if (li == 0) {
+            f32x4 Pr;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Pr[r] = al_s[0] * Mv[r];   // P_t = alpha_0 M[t][0]
+            *reinterpret_cast<f32x4 *>(rec + 528 + 4 * g) = Pr;
+        }
+        if (g == 3) rec[544 + li] = Mv[3];                         // D[s] = M[15][s]
+    }
+}
+
+// ---------------------------------------------------------------------------
+// State pass.  Block b_id -> (head, quarter): the four quarters of a head get
+// indices equal modulo 8, so they run on one XCD and share its L2 for the
+// head's workspace records and k, q rows.
+__global__ void __launch_bounds__(256) split_kernel(StepArgs a, const float *ws, int nc) {
+    __shared__ __align__(16) float k_s[2][kC * kKS], q_s[2][kC * kKS];
+    __shared__ f32x4 x_s[4][2][64];   // partial U, W of each wave
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l = tid & 63, g = l >> 4, li = l & 15;
+    const int half = w & 1, strip = w >> 1;
+
+    const int nheads = a.batch * a.nv;
+    const int full = nheads / 8 * 8;
+    int head, quarter;
+    {
+        const int bid = blockIdx.x;
+        if (bid < full * 4) {
+            const int r = bid & 31;
+            head = (bid >> 5) * 8 + (r & 7);
+            quarter = r >> 3;
+        } else {
+            const int r = bid - full * 4, rem = nheads - full;
+            head = full + r % rem;
+            quarter = r / rem;
+        }
+    }
+    const int b = head / a.nv;
+    const int h = head - b * a.nv;
+    const int kh = h % a.nk;
+    const int T = a.seq_len;
+    const int64_t row_base = (int64_t)b * T;
+    const int row = 32 * quarter + 16 * strip + li;          // state row (value index)
+    float *srow = static_cast<float *>(a.state) + (int64_t)b * a.pitch + (int64_t)h * (kD * kD) +
+                  (int64_t)row * kD + 64 * half + 4 * g;
+    const int64_t vcol = (int64_t)h * kD + row;
+    const float *wsh = ws + (int64_t)head * nc * kSeqRec;
+
+    // The true state is gam * S; S[m][r] = S[row][64 half + 16 m + 4 g + r].
+    f32x4 S[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) S[m] = *reinterpret_cast<const f32x4 *>(srow + 16 * m);
+    float gam = 1.0f;
+
+    // k and q of a chunk: pieces f = tid + 256 u (u = 0, 1), token f >> 5 =
+    // tid / 32 + 8 u, columns (tid % 32) * 4.  Per-lane base pointers are
+    // formed once; a whole chunk then adds a uniform offset per row.  Rows
+    // past T (the tail chunk and the chunks after it) are clamped to T - 1:
+    // the pre-pass gives those tokens beta 0 and alpha 1, and their k only
+    // meets a zero coefficient.
+    const int tl = tid >> 5;
+    const float *kb = a.k + (row_base + tl) * a.qk_stride + (int64_t)kh * kD + (tid & 31) * 4;
+    const float *qb = a.q + (kb - a.k);
+    f32x4 pk[2], pq[2];   // vector-typed so they stay in registers
+    auto prefetch_kq = [&](int c) {
+        const int t0 = c * kC;
+        if (t0 + kC <= T) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int64_t off = (int64_t)(t0 + 8 * u) * a.qk_stride;
+                pk[u] = *reinterpret_cast<const f32x4 *>(kb + off);
+                pq[u] = *reinterpret_cast<const f32x4 *>(qb + off);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int t = t0 + tl + 8 * u < T ? t0 + 8 * u : T - 1 - tl;
+                const int64_t off = (int64_t)t * a.qk_stride;
+                pk[u] = *reinterpret_cast<const f32x4 *>(kb + off);
+                pq[u] = *reinterpret_cast<const f32x4 *>(qb + off);
+            }
+        }
+    };
+    auto stage = [&](int c) {
+        const int bb = c & 1;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int f = tid + 256 * u;
+            *reinterpret_cast<f32x4 *>(&k_s[bb][(f >> 5) * kKS + (f & 31) * 4]) = pk[u];
+            *reinterpret_cast<f32x4 *>(&q_s[bb][(f >> 5) * kKS + (f & 31) * 4]) = pq[u];
+        }
+    };
+    // per-chunk data of the lane: v of its row for tokens 4g .. 4g+3, and the
+    // workspace record (T[li][4g..], G[li][4g..], beta, P, D at 4g.., P_15)
+    const float *vb = a.v + (row_base + 4 * g) * a.v_stride + vcol;
+    const int lrec = li * kC + 4 * g;
+    float vv[4];
+    f32x4 Tr, Gr, Br, Pr, Dr;
+    float Plast;
+    auto load_chunk = [&](int c) {
+        const int t0 = c * kC;
+        if (t0 + kC <= T) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) vv[r] = vb[(int64_t)(t0 + r) * a.v_stride];
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = t0 + 4 * g + r < T ? t0 + r : T - 1 - 4 * g;
+                vv[r] = vb[(int64_t)t * a.v_stride];
+            }
+        }
+        const float *rec = wsh + (int64_t)(c < nc ? c : nc - 1) * kSeqRec;   // uniform
+        Tr = *reinterpret_cast<const f32x4 *>(rec + lrec);
+        Gr = *reinterpret_cast<const f32x4 *>(rec + 256 + lrec);
+        Br = *reinterpret_cast<const f32x4 *>(rec + 512 + 4 * g);
+        Pr = *reinterpret_cast<const f32x4 *>(rec + 528 + 4 * g);
+        Dr = *reinterpret_cast<const f32x4 *>(rec + 544 + 4 * g);
+        Plast = rec[528 + kC - 1];
+    };
+
+    // Prologue: chunk 0 staged; chunk 1's k, q and chunk 0's v and record in flight.
+    prefetch_kq(0);
+    stage(0);
+    // drain every load (the state included) so that no conservative vmcnt wait
+    // lands inside the chunk loop
+    __builtin_amdgcn_s_waitcnt(0);
+    prefetch_kq(1);
+    load_chunk(0);
+    __syncthreads();
+
+    float *ob = static_cast<float *>(a.out) + (row_base + 4 * g) * a.out_stride + vcol;
+    for (int c = 0; c < nc; ++c) {
+        const int bb = c & 1;
+        const int t0 = c * kC;
+        const int nt = T - t0 < kC ? T - t0 : kC;
+        // partial U^T = K S^T and W^T = Q S^T over this wave's 64 columns
+        f32x4 Ua = f32x4{0.f, 0.f, 0.f, 0.f}, Ub = Ua, Wa = Ua, Wb = Ua;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int col = 64 * half + 16 * m + 4 * g;
+            const f32x4 ka = *reinterpret_cast<const f32x4 *>(&k_s[bb][li * kKS + col]);
+            const f32x4 qa = *reinterpret_cast<const f32x4 *>(&q_s[bb][li * kKS + col]);
+#pragma unroll
+            for (int r = 0; r < 4; r += 2) {
+                Ua = mfma(ka[r], S[m][r], Ua);
+                Wa = mfma(qa[r], S[m][r], Wa);
+                Ub = mfma(ka[r + 1], S[m][r + 1], Ub);
+                Wb = mfma(qa[r + 1], S[m][r + 1], Wb);
+            }
+        }
+        const f32x4 Up = Ua + Ub, Wp = Wa + Wb;
+        x_s[w][0][l] = Up;
+        x_s[w][1][l] = Wp;
+        __syncthreads();   // partials visible; every wave is past chunk c - 1
+        // the pair's sums (addition commutes, so both halves hold the same U, W)
+        const f32x4 U = Up + x_s[w ^ 1][0][l];
+        const f32x4 W = Wp + x_s[w ^ 1][1][l];
+        // chunk c + 1 into the buffer chunk c - 1 used (rows past the end are
+        // staged too, into a buffer no one reads)
+        stage(c + 1);
+
+        // R = beta (v - P gam U);  C' = T R;  O = P gam W + G C'
+        if (nt < kC) {   // tail chunk: tokens past T read a clamped row
+#pragma unroll
+            for (int r = 0; r < 4; ++r) vv[r] = 4 * g + r < nt ? vv[r] : 0.0f;
+        }
+        f32x4 R, O;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float pg = Pr[r] * gam;
+            R[r] = Br[r] * (vv[r] - pg * U[r]);
+            O[r] = pg * W[r];
+        }
+        f32x4 c0 = f32x4{0.f, 0.f, 0.f, 0.f}, c1 = c0;
+        c0 = mfma(Tr[0], R[0], c0);
+        c1 = mfma(Tr[1], R[1], c1);
+        c0 = mfma(Tr[2], R[2], c0);
+        c1 = mfma(Tr[3], R[3], c1);
+        f32x4 Cp = c0 + c1;
+        f32x4 o1 = f32x4{0.f, 0.f, 0.f, 0.f};
+        O = mfma(Gr[0], Cp[0], O);
+        o1 = mfma(Gr[1], Cp[1], o1);
+        O = mfma(Gr[2], Cp[2], O);
+        o1 = mfma(Gr[3], Cp[3], o1);
+        O += o1;
+        // each half stores two of the lane's four tokens
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+            const int r = 2 * half + rr;
+            if (nt == kC || 4 * g + r < nt) ob[(int64_t)(t0 + r) * a.out_stride] = O[r] * a.scale;
+        }
+
+        // gam S -> P_15 gam S + K^T (C' diag(D))^T, the decay kept in gam while
+        // it stays in [2^-60, 2^60] and folded into S otherwise
+        float gnew = gam * Plast;
+        float cscale;
+        if (gnew >= 0x1p-60f && gnew <= 0x1p60f) {
+            cscale = 1.0f / gnew;
+        } else {
+            const float f = gnew;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) S[m] *= f;
+            gnew = 1.0f;
+            cscale = 1.0f;
+        }
+        gam = gnew;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Cp[r] *= Dr[r] * cscale;
+        const float *kc = &k_s[bb][4 * g * kKS + 64 * half + li];   // k of token 4g + s4, column 64 half + 16 m + li
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) S[m] = mfma(kc[s4 * kKS + 16 * m], Cp[s4], S[m]);
+
+        // loads for the next chunks go out after this chunk's stores
+        prefetch_kq(c + 2);
+        load_chunk(c + 1);
+        __syncthreads();   // chunk c + 1 staged; every read of chunk c's buffers done
+    }
+
+#pragma unroll
+    for (int m = 0; m < 4; ++m) *reinterpret_cast<f32x4 *>(srow + 16 * m) = S[m] * gam;
+}
+
+hipError_t launch_seq_split(const StepArgs &a, float *ws, hipStream_t stream) {
+    const int nc = (a.seq_len + kC - 1) / kC;
+    const int64_t items = (int64_t)a.batch * a.nk * nc;
+    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)items), dim3(64), 0, stream, a, ws, nc);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const unsigned grid = (unsigned)((int64_t)a.batch * a.nv * 4);
+    hipLaunchKernelGGL(split_kernel, dim3(grid), dim3(256), 0, stream, a, (const float *)ws, nc);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

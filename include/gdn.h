@@ -185,6 +185,47 @@ gdn_status gdn_recurrence_seq(float *state, int64_t state_seq_stride,
                               int32_t num_v_heads, int32_t k_dim, int32_t v_dim, void *stream);
 
 /*
+ * gdn_recurrence_seq_ws -- gdn_recurrence_seq with a caller-provided device
+ * workspace.  Same operation, arguments, layouts and results (within the fp32
+ * tolerance; the summation order differs).  For k_dim == v_dim == 128 and the
+ * raw output (z == NULL) it runs in two launches: a pre-pass forms, for every
+ * (sequence, value head, 16-token chunk), the input-only quantities of the
+ * chunked form of the recurrence (the inverse of the chunk's unit lower
+ * triangular system, the decayed k.q matrix, beta and the decay products) into
+ * the workspace, and the state pass then splits each head over four
+ * workgroups.  Any other call ignores the workspace (it may be NULL) and runs
+ * as gdn_recurrence_seq.  Source: metrale ssm_gdn_a.rs, launcher
+ * `gdn_prefill_regresident` (the operation); the chunked form is exact algebra
+ * on logicaffeine gdn.rs `gdn_step`.
+ *   workspace        device memory of at least gdn_seq_workspace_bytes(...)
+ *                    bytes, 16-byte aligned, overlapping no other argument
+ *                    (GDN_ERR_NULL, GDN_ERR_ARG if smaller, GDN_ERR_STRIDE if
+ *                    misaligned, GDN_ERR_ALIAS).  Owned by the caller; its
+ *                    contents are scratch, written and read within the call
+ *                    (calls that share a workspace must be ordered on one
+ *                    stream).
+ *   workspace_bytes  its size in bytes.
+ */
+gdn_status gdn_recurrence_seq_ws(float *state, int64_t state_seq_stride,
+                                 const float *q, const float *k, int64_t qk_stride,
+                                 const float *v, int64_t v_stride,
+                                 const float *alpha, const float *beta, int64_t ab_stride,
+                                 const float *z, int64_t z_stride, const float *norm_weight,
+                                 float eps, float *out, int64_t out_stride,
+                                 int32_t batch, int32_t seq_len, int32_t num_k_heads,
+                                 int32_t num_v_heads, int32_t k_dim, int32_t v_dim,
+                                 void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * gdn_seq_workspace_bytes -- bytes of workspace gdn_recurrence_seq_ws uses for
+ * this shape: batch * num_v_heads * ceil(seq_len / 16) * 2304 when
+ * k_dim == v_dim == 128, else 0 (no workspace used).  -1 for a negative or
+ * overflowing shape.  Host-only; touches no device.
+ */
+int64_t gdn_seq_workspace_bytes(int32_t batch, int32_t seq_len, int32_t num_v_heads,
+                                int32_t k_dim, int32_t v_dim);
+
+/*
  * gdn_decode_verify -- num_tokens (1..GDN_VERIFY_MAX_TOKENS) consecutive tokens
  * per sequence in one launch, keeping the state after every token but the last
  * for rollback: when a speculative (draft) token is rejected, the state after

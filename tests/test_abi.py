@@ -33,7 +33,7 @@ def _declared():
 def test_header_declarations_found():
     names = _declared()
     assert "gdn_decode" in names and "gdn_decode_verify" in names
-    assert len(names) == 11, names
+    assert len(names) == 13, names
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -154,6 +154,46 @@ def test_seq_validation(lib):
     assert seq(lib, vs=NV * D - 4) == 3
     p = _bases()
     assert seq(lib, out=p["q"]) == 5
+
+
+def seq_ws(lib, **kw):
+    """gdn_recurrence_seq_ws at D = 128 (the shape that uses the workspace)."""
+    p = _bases()
+    d, slot = 128, NV * 128 * 128
+    need = B * NV * 1 * 2304
+    a = dict(state=p["state"], pitch=slot, q=p["q"], k=p["k"], qk=NK * d, v=p["v"], vs=NV * d,
+             al=p["alpha"], be=p["beta"], ab=NV, z=None, zs=0, gn=None, eps=1e-6,
+             out=p["out"], os=NV * d, B=B, T=5, nk=NK, nv=NV, dk=d, dv=d,
+             ws=A + 10 * (1 << 24), wsb=need)
+    a.update(kw)
+    return lib.gdn_recurrence_seq_ws(a["state"], a["pitch"], a["q"], a["k"], a["qk"], a["v"],
+                                     a["vs"], a["al"], a["be"], a["ab"], a["z"], a["zs"],
+                                     a["gn"], a["eps"], a["out"], a["os"], a["B"], a["T"],
+                                     a["nk"], a["nv"], a["dk"], a["dv"], a["ws"], a["wsb"], None)
+
+
+def test_seq_workspace_bytes(lib):
+    assert lib.gdn_seq_workspace_bytes(4, 4096, 48, 128, 128) == 4 * 48 * 256 * 2304
+    assert lib.gdn_seq_workspace_bytes(2, 16, 4, 128, 128) == 2 * 4 * 1 * 2304
+    assert lib.gdn_seq_workspace_bytes(2, 17, 4, 128, 128) == 2 * 4 * 2 * 2304
+    assert lib.gdn_seq_workspace_bytes(2, 0, 4, 128, 128) == 0
+    assert lib.gdn_seq_workspace_bytes(2, 17, 4, 64, 64) == 0      # no workspace used
+    assert lib.gdn_seq_workspace_bytes(-1, 5, 4, 128, 128) == -1
+
+
+def test_seq_ws_validation(lib):
+    p = _bases()
+    need = B * NV * 2304
+    assert seq_ws(lib, ws=None) == 1                      # needed at D = 128, raw output
+    assert seq_ws(lib, wsb=need - 4) == 8                 # smaller than gdn_seq_workspace_bytes
+    assert seq_ws(lib, ws=A + 10 * (1 << 24) + 4) == 3    # not 16-byte aligned
+    assert seq_ws(lib, ws=p["state"] + 64) == 5           # inside the state
+    assert seq_ws(lib, ws=p["q"]) == 5                    # over an input
+    assert seq_ws(lib, ws=p["out"] + 16) == 5             # over the output
+    assert seq_ws(lib, T=-1) == 2
+    assert seq_ws(lib, T=0, ws=None) == 0                 # empty: no launch, OK
+    assert seq_ws(lib, vs=NV * 128 - 4) == 3              # the plain call's checks come first
+    assert seq_ws(lib, out=p["q"], ws=None) == 5
 
 
 def test_verify_validation(lib):

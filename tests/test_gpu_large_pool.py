@@ -44,6 +44,12 @@ def g():
     return gdn
 
 
+@pytest.fixture(scope="module", params=["gdn_recurrence_seq", "gdn_recurrence_seq_ws"])
+def seq(g, request):
+    """Both sequence entry points: without and with the chunk workspace."""
+    return getattr(g, request.param)
+
+
 @pytest.fixture(autouse=True)
 def _release():
     yield
@@ -126,7 +132,7 @@ def test_large_pool_f16_state(g):
         assert tile_err(gs, ref16.view(np.float16).astype(np.float64), NV, D) < TOL_F16, b
 
 
-def test_large_pool_sequence(g):
+def test_large_pool_sequence(g, seq):
     """Three tokens per sequence through the chunked sequence kernel."""
     import torch
     T = 3
@@ -136,8 +142,8 @@ def test_large_pool_sequence(g):
     for b, r in SAMPLES.items():
         st[b] = dev(c.state[r])
     d = _tiled(c, T, ("q", "k", "v", "alpha", "beta"))
-    o = g.gdn_recurrence_seq(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"], seq_len=T,
-                             num_k_heads=NK, num_v_heads=NV, head_dim=D)
+    o = seq(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"], seq_len=T,
+            num_k_heads=NK, num_v_heads=NV, head_dim=D)
     got_o = host(o)
     for b, r in _checked():
         ref_st = _init_state(c, b, r)

@@ -35,6 +35,12 @@ def g():
     return gdn
 
 
+@pytest.fixture(scope="module", params=["gdn_recurrence_seq", "gdn_recurrence_seq_ws"])
+def seq(g, request):
+    """Both sequence entry points: without and with the chunk workspace."""
+    return getattr(g, request.param)
+
+
 def say(*a):
     print("[case]", *a, file=sys.stderr, flush=True)
 
@@ -243,7 +249,7 @@ def test_fp16_state_padded_pitch_raw_and_f32(g):
 
 # --------------------------------------------------------------------------- 5
 @pytest.mark.parametrize("init", ["zero", "normal"])
-def test_sequence_4096_tokens(g, init):
+def test_sequence_4096_tokens(g, seq, init):
     """B=4, T=4096, NV=48, NK=16, D=128: sampled heads through 4096 oracle steps
     (every token's output and the final state)."""
     c = inputs.config_case("sequence", state_init=init)
@@ -251,8 +257,8 @@ def test_sequence_4096_tokens(g, init):
     say("sequence", init, B, T)
     d = _dev_case(c)
     st = dev(c.state)
-    o = g.gdn_recurrence_seq(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"], seq_len=T,
-                             num_k_heads=NK, num_v_heads=NV, head_dim=D)
+    o = seq(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"], seq_len=T,
+            num_k_heads=NK, num_v_heads=NV, head_dim=D)
     heads = _sample_heads(B, NV, 6, 55 if init == "zero" else 56)
     ref_state = c.state.copy()
     ref = orc.seq_head_threaded(ref_state, c.q, c.k, c.v, c.alpha, c.beta, B=B, T=T, NK=NK,
@@ -283,15 +289,15 @@ def test_sequence_fused_norm_ragged(g):
     assert tile_err(host(st), ref_state, NV, D) < TOL_CHAIN
 
 
-def test_sequence_equals_chained_decode(g):
+def test_sequence_equals_chained_decode(g, seq):
     """T tokens in one sequence launch == T chained single-token launches (1e-4)."""
     B, T, NK, NV, D = 3, 20, 4, 8, 128
     c = inputs.make_case(58, B=B, NK=NK, NV=NV, D=D, T=T)
     say("seq == chained decode")
     d = _dev_case(c)
     st_seq = dev(c.state)
-    o_seq = host(g.gdn_recurrence_seq(st_seq, d["q"], d["k"], d["v"], d["alpha"], d["beta"],
-                                      seq_len=T, num_k_heads=NK, num_v_heads=NV, head_dim=D))
+    o_seq = host(seq(st_seq, d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                     seq_len=T, num_k_heads=NK, num_v_heads=NV, head_dim=D))
     st = dev(c.state)
     o_chain = np.zeros_like(o_seq)
     for t in range(T):
@@ -502,15 +508,15 @@ def test_batch_permutation_permutes_results_bitwise(g, kind):
     assert np.array_equal(s1, s0[perm])
 
 
-def test_empty_batch_and_length_are_noops(g):
+def test_empty_batch_and_length_are_noops(g, seq):
     import torch
     c = inputs.make_case(63, B=2, NK=2, NV=4, D=16, T=1)
     say("empty")
     d = _dev_case(c)
     st = dev(c.state)
     out = torch.full((2, 64), 7.0, device="cuda:0")
-    g.gdn_recurrence_seq(st, d["q"][:0], d["k"][:0], d["v"][:0], d["alpha"][:0], d["beta"][:0],
-                         out=out[:0], seq_len=0, num_k_heads=2, num_v_heads=4, head_dim=16)
+    seq(st, d["q"][:0], d["k"][:0], d["v"][:0], d["alpha"][:0], d["beta"][:0],
+        out=out[:0], seq_len=0, num_k_heads=2, num_v_heads=4, head_dim=16)
     e = torch.empty((0, 4 * 16 * 16), device="cuda:0")
     o = g.gdn_decode(e, d["q"][:0], d["k"][:0], d["v"][:0], d["alpha"][:0], d["beta"][:0],
                      num_k_heads=2, num_v_heads=4, head_dim=16)
@@ -679,7 +685,7 @@ def test_graph_replay_matches_eager(g):
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("T", [1, 15, 16, 17, 32, 33, 48])
 @pytest.mark.parametrize("norm", [False, True])
-def test_sequence_chunk_boundaries(g, D, T, norm):
+def test_sequence_chunk_boundaries(g, seq, D, T, norm):
     """Lengths around the 16-token chunk (and the two chunk buffers of the
     matrix-core kernel at D = 128): outputs and final state against the oracle."""
     B, NK, NV = 2, 2, 6
@@ -688,8 +694,8 @@ def test_sequence_chunk_boundaries(g, D, T, norm):
     d = _dev_case(c)
     st = dev(c.state)
     kw = dict(z=d["z"], norm_weight=d["gn"], eps=c.eps) if norm else dict(head_dim=D)
-    o = g.gdn_recurrence_seq(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"], seq_len=T,
-                             num_k_heads=NK, num_v_heads=NV, **kw)
+    o = seq(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"], seq_len=T,
+            num_k_heads=NK, num_v_heads=NV, **kw)
     ref_st = c.state.copy()
     okw = dict(z=c.z, gn=c.gn, eps=c.eps) if norm else {}
     ref = orc.seq(ref_st, c.q, c.k, c.v, c.alpha, c.beta, B=B, T=T, NK=NK, NV=NV, Dk=D, Dv=D, **okw)
@@ -698,7 +704,7 @@ def test_sequence_chunk_boundaries(g, D, T, norm):
 
 
 @pytest.mark.parametrize("D", [64, 128])
-def test_sequence_extreme_decay(g, D):
+def test_sequence_extreme_decay(g, seq, D):
     """Decays of exactly 0 (the state is forgotten), 1e-8 (the running decay
     product leaves any fixed exponent range within a few tokens), 1 (no decay)
     and ordinary values, mixed within chunks, with write strengths of 0 and 1
@@ -714,8 +720,8 @@ def test_sequence_extreme_decay(g, D):
     say("seq extreme decay", D)
     d = _dev_case(c)
     st = dev(c.state)
-    o = g.gdn_recurrence_seq(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"], seq_len=T,
-                             num_k_heads=NK, num_v_heads=NV, head_dim=D)
+    o = seq(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"], seq_len=T,
+            num_k_heads=NK, num_v_heads=NV, head_dim=D)
     ref_st = c.state.copy()
     ref = orc.seq(ref_st, c.q, c.k, c.v, c.alpha, c.beta, B=B, T=T, NK=NK, NV=NV, Dk=D, Dv=D)
     got_o, got_st = host(o), host(st)

@@ -30,6 +30,12 @@ def g():
     return gdn
 
 
+@pytest.fixture(scope="module", params=["gdn_recurrence_seq", "gdn_recurrence_seq_ws"])
+def seq(g, request):
+    """Both sequence entry points: without and with the chunk workspace."""
+    return getattr(g, request.param)
+
+
 def say(*a):
     print("[case]", *a, file=sys.stderr, flush=True)
 
@@ -59,7 +65,7 @@ def _pads_untouched(wide, st, NV, D):
 
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("norm", [False, True])
-def test_sequence_packed_rows(g, D, norm):
+def test_sequence_packed_rows(g, seq, D, norm):
     """T = 37 tokens (two full 16-token chunks and a ragged one) on packed rows;
     D = 128 runs the chunked matrix-core kernel, D = 64 the token loop."""
     B, NK, NV, T = 3, 2, 6, 37
@@ -67,9 +73,9 @@ def test_sequence_packed_rows(g, D, norm):
     say("sequence packed rows", D, "norm" if norm else "raw")
     d = _packed(c, B * T)
     st = dev(c.state)
-    g.gdn_recurrence_seq(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"],
-                         d["z"] if norm else None, dev(c.gn) if norm else None, c.eps,
-                         out=d["out"], seq_len=T, num_k_heads=NK, num_v_heads=NV, head_dim=D)
+    seq(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+        d["z"] if norm else None, dev(c.gn) if norm else None, c.eps,
+        out=d["out"], seq_len=T, num_k_heads=NK, num_v_heads=NV, head_dim=D)
     ref_st = c.state.copy()
     kw = dict(z=c.z, gn=c.gn, eps=c.eps) if norm else {}
     ref = orc.seq(ref_st, c.q, c.k, c.v, c.alpha, c.beta, B=B, T=T, NK=NK, NV=NV, Dk=D, Dv=D, **kw)
