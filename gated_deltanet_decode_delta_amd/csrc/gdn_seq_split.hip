@@ -39,7 +39,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kD = 128;
 constexpr int kC = 16;            // tokens per chunk
 constexpr int kKS = kD + 4;       // LDS row stride (floats) of k / q
-constexpr int kTS = kC + 1;       // LDS row stride of 16x16 matrices in the pre-pass
+constexpr int kTS = kC + 4;       // LDS row stride of 16x16 matrices in the pre-pass (16-byte rows)
 
 __device__ __forceinline__ f32x4 mfma(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -57,13 +57,16 @@ __device__ __forceinline__ float dpp_from_above(float x) {
 
 // ---------------------------------------------------------------------------
 // Pre-pass: one wave per (sequence b, key head kh, chunk c).  Tokens past T
-// get alpha 1, beta 0 and zero k, q, so they change nothing.
+// get alpha 1, beta 0 and zero k, q, so they change nothing.  k and q go
+// straight from global memory into the matrix-core operand layout (lane (g, li)
+// holds row li, columns 16m + 4g .. +3), and the alpha, beta loads of up to 16
+// value heads are issued together, ahead of the work on them.
 __global__ void __launch_bounds__(64) prep_kernel(StepArgs a, float *ws, int nc) {
-    __shared__ __align__(16) float k_s[kC * kKS], q_s[kC * kKS];
-    __shared__ float m_s[kC * kTS];    // M[t][s]
-    __shared__ float a_s[kC * kTS];    // a_s[s][t] = A[t][s]
-    __shared__ float t_s[kC * kTS];    // T[t][s]
-    __shared__ float al_s[kC + 1], be_s[kC];
+    constexpr int kHG = 16;   // value heads whose alpha, beta are staged at once
+    __shared__ __align__(16) float m_s[kC * kTS];   // M[t][s]
+    __shared__ __align__(16) float a_s[kC * kTS];   // a_s[s][t] = A[t][s]
+    __shared__ __align__(16) float t_s[kC * kTS];   // T[t][s]
+    __shared__ float al_s[kHG][kC + 1], be_s[kHG][kC];
 
     const int l = threadIdx.x, g = l >> 4, li = l & 15;
     const int item = blockIdx.x;
@@ -74,99 +77,120 @@ __global__ void __launch_bounds__(64) prep_kernel(StepArgs a, float *ws, int nc)
     const int T = a.seq_len;
     const int t0 = c * kC;
     const int64_t row_base = (int64_t)b * T;
+    const int rep = a.nv / a.nk;
 
+    const bool rok = t0 + li < T;
+    const int64_t roff = (row_base + (rok ? t0 + li : T - 1)) * a.qk_stride + (int64_t)kh * kD + 4 * g;
+    f32x4 kr[kD / 16], qr[kD / 16];
 #pragma unroll
-    for (int u = 0; u < kC * kD / 4 / 64; ++u) {
-        const int f = l + 64 * u;
-        const int t = f >> 5, col = (f & 31) * 4;
-        const bool ok = t0 + t < T;
-        const int64_t off = (row_base + (ok ? t0 + t : T - 1)) * a.qk_stride + (int64_t)kh * kD + col;
-        const float4 kx = *reinterpret_cast<const float4 *>(a.k + off);
-        const float4 qx = *reinterpret_cast<const float4 *>(a.q + off);
-        *reinterpret_cast<float4 *>(&k_s[t * kKS + col]) =
-            make_float4(ok ? kx.x : 0.f, ok ? kx.y : 0.f, ok ? kx.z : 0.f, ok ? kx.w : 0.f);
-        *reinterpret_cast<float4 *>(&q_s[t * kKS + col]) =
-            make_float4(ok ? qx.x : 0.f, ok ? qx.y : 0.f, ok ? qx.z : 0.f, ok ? qx.w : 0.f);
+    for (int m = 0; m < kD / 16; ++m) {
+        kr[m] = *reinterpret_cast<const f32x4 *>(a.k + roff + 16 * m);
+        qr[m] = *reinterpret_cast<const f32x4 *>(a.q + roff + 16 * m);
     }
-    __syncthreads();
+    // alpha, beta of value heads m0 .. m0 + 15: entry e = l + 64 j is head e / 16, token e % 16
+    float ar[4], br[4];
+    auto load_ab = [&](int m0) {
+        const int ng = rep - m0 < kHG ? rep - m0 : kHG;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = l + 64 * j, m = e >> 4, t = e & 15;
+            if (m < ng) {
+                const bool ok = t0 + t < T;
+                const int64_t rr = (row_base + (ok ? t0 + t : T - 1)) * a.ab_stride + kh + (int64_t)(m0 + m) * a.nk;
+                const float ax = a.alpha[rr], bx = a.beta[rr];
+                ar[j] = ok ? ax : 1.0f;
+                br[j] = ok ? bx : 0.0f;
+            }
+        }
+    };
+    auto store_ab = [&](int m0) {
+        const int ng = rep - m0 < kHG ? rep - m0 : kHG;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = l + 64 * j, m = e >> 4, t = e & 15;
+            if (m < ng) {
+                al_s[m][t] = ar[j];
+                be_s[m][t] = br[j];
+            }
+        }
+    };
+    load_ab(0);
+    if (!rok) {
+#pragma unroll
+        for (int m = 0; m < kD / 16; ++m) {
+            kr[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+            qr[m] = kr[m];
+        }
+    }
     // lane (g, li), register r: KK[r] = k_{4g+r}.k_{li}, KQ[r] = k_{4g+r}.q_{li}
     f32x4 K0 = f32x4{0.f, 0.f, 0.f, 0.f}, K1 = K0, Q0 = K0, Q1 = K0;
 #pragma unroll
     for (int m = 0; m < kD / 16; ++m) {
-        const f32x4 ka = *reinterpret_cast<const f32x4 *>(&k_s[li * kKS + 16 * m + 4 * g]);
-        const f32x4 qa = *reinterpret_cast<const f32x4 *>(&q_s[li * kKS + 16 * m + 4 * g]);
-        K0 = mfma(ka[0], ka[0], K0);
-        Q0 = mfma(ka[0], qa[0], Q0);
-        K1 = mfma(ka[1], ka[1], K1);
-        Q1 = mfma(ka[1], qa[1], Q1);
-        K0 = mfma(ka[2], ka[2], K0);
-        Q0 = mfma(ka[2], qa[2], Q0);
-        K1 = mfma(ka[3], ka[3], K1);
-        Q1 = mfma(ka[3], qa[3], Q1);
+        K0 = mfma(kr[m][0], kr[m][0], K0);
+        Q0 = mfma(kr[m][0], qr[m][0], Q0);
+        K1 = mfma(kr[m][1], kr[m][1], K1);
+        Q1 = mfma(kr[m][1], qr[m][1], Q1);
+        K0 = mfma(kr[m][2], kr[m][2], K0);
+        Q0 = mfma(kr[m][2], qr[m][2], Q0);
+        K1 = mfma(kr[m][3], kr[m][3], K1);
+        Q1 = mfma(kr[m][3], qr[m][3], Q1);
     }
     const f32x4 KK = K0 + K1, KQ = Q0 + Q1;
 
-    const int rep = a.nv / a.nk;
-    for (int m = 0; m < rep; ++m) {
-        const int h = kh + m * a.nk;   // tiled pairing: value heads g, g + NK, ...
-        {
-            const bool ok = t0 + li < T;
-            const int64_t rr = row_base + (ok ? t0 + li : T - 1);
-            const float ax = a.alpha[rr * a.ab_stride + h];
-            const float bx = a.beta[rr * a.ab_stride + h];
-            __syncthreads();   // the previous head's reads of al_s .. t_s are done
-            if (g == 0) {
-                al_s[li] = ok ? ax : 1.0f;
-                be_s[li] = ok ? bx : 0.0f;
+    for (int m0 = 0; m0 < rep; m0 += kHG) {
+        __syncthreads();   // the previous group's reads of al_s, be_s are done
+        store_ab(m0);
+        if (m0 + kHG < rep) load_ab(m0 + kHG);
+        __syncthreads();
+        const int ng = rep - m0 < kHG ? rep - m0 : kHG;
+        for (int mm = 0; mm < ng; ++mm) {
+            const int h = kh + (m0 + mm) * a.nk;   // tiled pairing: value heads kh, kh + NK, ...
+            // M[4g + r][li] by suffix products along the DPP row (no division)
+            f32x4 Mv;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * g + r;
+                float x = li < t ? al_s[mm][li + 1] : 1.0f;
+                x *= dpp_from_above<1>(x);
+                x *= dpp_from_above<2>(x);
+                x *= dpp_from_above<4>(x);
+                x *= dpp_from_above<8>(x);
+                Mv[r] = t >= li ? x : 0.0f;
+                m_s[t * kTS + li] = Mv[r];
+                a_s[li * kTS + t] = li < t ? be_s[mm][t] * Mv[r] * KK[r] : 0.0f;
             }
             __syncthreads();
+            // T = (I + A)^{-1}, column li per lane: column-oriented forward
+            // substitution, rows of the transposed A read four at a time
+            float x[kC];
+#pragma unroll
+            for (int t = 0; t < kC; ++t) x[t] = t == li ? 1.0f : 0.0f;
+#pragma unroll
+            for (int s2 = 0; s2 < kC - 1; ++s2) {
+#pragma unroll
+                for (int t4 = (s2 + 1) / 4; t4 < kC / 4; ++t4) {
+                    const f32x4 av = *reinterpret_cast<const f32x4 *>(&a_s[s2 * kTS + 4 * t4]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (4 * t4 + e > s2) x[4 * t4 + e] = fmaf(-av[e], x[s2], x[4 * t4 + e]);
+                }
+            }
+            if (g == 0) {
+#pragma unroll
+                for (int t = 0; t < kC; ++t) t_s[t * kTS + li] = x[t];
+            }
+            __syncthreads();
+            // workspace record: T row-major, G row-major, beta, P, D
+            float *rec = ws + (((int64_t)b * a.nv + h) * nc + c) * kSeqRec;
+            const f32x4 Tr = *reinterpret_cast<const f32x4 *>(&t_s[li * kTS + 4 * g]);
+            const f32x4 Mr = *reinterpret_cast<const f32x4 *>(&m_s[li * kTS + 4 * g]);
+            *reinterpret_cast<f32x4 *>(rec + li * kC + 4 * g) = Tr;
+            *reinterpret_cast<f32x4 *>(rec + 256 + li * kC + 4 * g) = Mr * KQ;   // G[li][4g+r] = M[li][4g+r] k_{4g+r}.q_{li}
+            if (g == 0) rec[512 + li] = be_s[mm][li];
+            if (li == 0) *reinterpret_cast<f32x4 *>(rec + 528 + 4 * g) = al_s[mm][0] * Mv;   // P_t = alpha_0 M[t][0]
+            if (g == 3) rec[544 + li] = Mv[3];                                             // D[s] = M[15][s]
+            __syncthreads();   // m_s, a_s, t_s free for the next head
         }
-        // M[4g + r][li] by suffix products along the DPP row (no division)
-        f32x4 Mv;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 4 * g + r;
-            float x = li < t ? al_s[li + 1] : 1.0f;
-            x *= dpp_from_above<1>(x);
-            x *= dpp_from_above<2>(x);
-            x *= dpp_from_above<4>(x);
-            x *= dpp_from_above<8>(x);
-            Mv[r] = t >= li ? x : 0.0f;
-            m_s[t * kTS + li] = Mv[r];
-            a_s[li * kTS + t] = li < t ? be_s[t] * Mv[r] * KK[r] : 0.0f;
-        }
-        __syncthreads();
-        // T = (I + A)^{-1}, column li per lane (column-oriented forward substitution)
-        float x[kC];
-#pragma unroll
-        for (int t = 0; t < kC; ++t) x[t] = t == li ? 1.0f : 0.0f;
-#pragma unroll
-        for (int s2 = 0; s2 < kC - 1; ++s2)
-#pragma unroll
-            for (int t = s2 + 1; t < kC; ++t) x[t] = fmaf(-a_s[s2 * kTS + t], x[s2], x[t]);
-        if (g == 0) {
-#pragma unroll
-            for (int t = 0; t < kC; ++t) t_s[t * kTS + li] = x[t];
-        }
-        __syncthreads();
-        // workspace record: T row-major, G row-major, beta, P, D
-        float *rec = ws + (((int64_t)b * a.nv + h) * nc + c) * kSeqRec;
-        f32x4 Tr, Gr;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            Tr[r] = t_s[li * kTS + 4 * g + r];
-            Gr[r] = m_s[li * kTS + 4 * g + r] * KQ[r];   // G[li][4g+r] = M[li][4g+r] k_{4g+r}.q_{li}
-        }
-        *reinterpret_cast<f32x4 *>(rec + li * kC + 4 * g) = Tr;
-        *reinterpret_cast<f32x4 *>(rec + 256 + li * kC + 4 * g) = Gr;
-        if (g == 0) rec[512 + li] = be_s[li];
-        if (li == 0) {
-            f32x4 Pr;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Pr[r] = al_s[0] * Mv[r];   // P_t = alpha_0 M[t][0]
-            *reinterpret_cast<f32x4 *>(rec + 528 + 4 * g) = Pr;
-        }
-        if (g == 3) rec[544 + li] = Mv[3];                         // D[s] = M[15][s]
     }
 }
 
@@ -346,11 +370,16 @@ __global__ void __launch_bounds__(256) split_kernel(StepArgs a, const float *ws,
         O = mfma(Gr[2], Cp[2], O);
         o1 = mfma(Gr[3], Cp[3], o1);
         O += o1;
-        // each half stores two of the lane's four tokens
+        // each half stores two of the lane's four tokens (a uniform branch, so
+        // the registers are picked at compile time)
+        if (half == 0) {
 #pragma unroll
-        for (int rr = 0; rr < 2; ++rr) {
-            const int r = 2 * half + rr;
-            if (nt == kC || 4 * g + r < nt) ob[(int64_t)(t0 + r) * a.out_stride] = O[r] * a.scale;
+            for (int r = 0; r < 2; ++r)
+                if (nt == kC || 4 * g + r < nt) ob[(int64_t)(t0 + r) * a.out_stride] = O[r] * a.scale;
+        } else {
+#pragma unroll
+            for (int r = 2; r < 4; ++r)
+                if (nt == kC || 4 * g + r < nt) ob[(int64_t)(t0 + r) * a.out_stride] = O[r] * a.scale;
         }
 
         // gam S -> P_15 gam S + K^T (C' diag(D))^T, the decay kept in gam while
