@@ -201,6 +201,7 @@ __global__ void __launch_bounds__(64) prep_kernel(StepArgs a, float *ws, int nc)
 __global__ void __launch_bounds__(256) split_kernel(StepArgs a, const float *ws, int nc) {
     __shared__ __align__(16) float k_s[2][kC * kKS], q_s[2][kC * kKS];
     __shared__ f32x4 x_s[4][2][64];   // partial U, W of each wave
+    __shared__ f32x4 c_s[2][64];      // C' of each strip
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -339,46 +340,46 @@ __global__ void __launch_bounds__(256) split_kernel(StepArgs a, const float *ws,
         x_s[w][0][l] = Up;
         x_s[w][1][l] = Wp;
         __syncthreads();   // partials visible; every wave is past chunk c - 1
-        // the pair's sums (addition commutes, so both halves hold the same U, W)
-        const f32x4 U = Up + x_s[w ^ 1][0][l];
-        const f32x4 W = Wp + x_s[w ^ 1][1][l];
         // chunk c + 1 into the buffer chunk c - 1 used (rows past the end are
-        // staged too, into a buffer no one reads)
+        // staged too, into a buffer no one reads); visible after the next barrier
         stage(c + 1);
-
-        // R = beta (v - P gam U);  C' = T R;  O = P gam W + G C'
-        if (nt < kC) {   // tail chunk: tokens past T read a clamped row
-#pragma unroll
-            for (int r = 0; r < 4; ++r) vv[r] = 4 * g + r < nt ? vv[r] : 0.0f;
-        }
-        f32x4 R, O;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float pg = Pr[r] * gam;
-            R[r] = Br[r] * (vv[r] - pg * U[r]);
-            O[r] = pg * W[r];
-        }
-        f32x4 c0 = f32x4{0.f, 0.f, 0.f, 0.f}, c1 = c0;
-        c0 = mfma(Tr[0], R[0], c0);
-        c1 = mfma(Tr[1], R[1], c1);
-        c0 = mfma(Tr[2], R[2], c0);
-        c1 = mfma(Tr[3], R[3], c1);
-        f32x4 Cp = c0 + c1;
-        f32x4 o1 = f32x4{0.f, 0.f, 0.f, 0.f};
-        O = mfma(Gr[0], Cp[0], O);
-        o1 = mfma(Gr[1], Cp[1], o1);
-        O = mfma(Gr[2], Cp[2], O);
-        o1 = mfma(Gr[3], Cp[3], o1);
-        O += o1;
-        // each half stores two of the lane's four tokens (a uniform branch, so
-        // the registers are picked at compile time)
+        // The strip's chain is split between its halves: half 0 forms
+        // R = beta (v - P gam U) and C' = T R and passes C' on through LDS;
+        // half 1 forms O = P gam W + G C' and stores the four tokens.  Both
+        // update their own columns with C'.
+        f32x4 Cp, O;
         if (half == 0) {
+            const f32x4 U = Up + x_s[w ^ 1][0][l];
+            if (nt < kC) {   // tail chunk: tokens past T read a clamped row
 #pragma unroll
-            for (int r = 0; r < 2; ++r)
-                if (nt == kC || 4 * g + r < nt) ob[(int64_t)(t0 + r) * a.out_stride] = O[r] * a.scale;
+                for (int r = 0; r < 4; ++r) vv[r] = 4 * g + r < nt ? vv[r] : 0.0f;
+            }
+            f32x4 R;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) R[r] = Br[r] * (vv[r] - Pr[r] * gam * U[r]);
+            f32x4 c0 = f32x4{0.f, 0.f, 0.f, 0.f}, c1 = c0;
+            c0 = mfma(Tr[0], R[0], c0);
+            c1 = mfma(Tr[1], R[1], c1);
+            c0 = mfma(Tr[2], R[2], c0);
+            c1 = mfma(Tr[3], R[3], c1);
+            Cp = c0 + c1;
+            c_s[strip][l] = Cp;
         } else {
+            const f32x4 W = Wp + x_s[w ^ 1][1][l];
 #pragma unroll
-            for (int r = 2; r < 4; ++r)
+            for (int r = 0; r < 4; ++r) O[r] = Pr[r] * gam * W[r];
+        }
+        __syncthreads();   // C' visible; chunk c + 1 staged; every read of chunk c - 1's buffers done
+        if (half == 1) {
+            Cp = c_s[strip][l];
+            f32x4 o1 = f32x4{0.f, 0.f, 0.f, 0.f};
+            O = mfma(Gr[0], Cp[0], O);
+            o1 = mfma(Gr[1], Cp[1], o1);
+            O = mfma(Gr[2], Cp[2], O);
+            o1 = mfma(Gr[3], Cp[3], o1);
+            O += o1;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
                 if (nt == kC || 4 * g + r < nt) ob[(int64_t)(t0 + r) * a.out_stride] = O[r] * a.scale;
         }
 
@@ -407,7 +408,6 @@ __global__ void __launch_bounds__(256) split_kernel(StepArgs a, const float *ws,
         // loads for the next chunks go out after this chunk's stores
         prefetch_kq(c + 2);
         load_chunk(c + 1);
-        __syncthreads();   // chunk c + 1 staged; every read of chunk c's buffers done
     }
 
 #pragma unroll
