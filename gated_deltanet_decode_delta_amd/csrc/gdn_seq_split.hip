@@ -242,28 +242,22 @@ __global__ void __launch_bounds__(256) split_kernel(StepArgs a, const float *ws,
 
     // k and q of a chunk: pieces f = tid + 256 u (u = 0, 1), token f >> 5 =
     // tid / 32 + 8 u, columns (tid % 32) * 4.  Per-lane base pointers are
-    // formed once; a whole chunk then adds a uniform offset per row.  Rows
-    // past T (the tail chunk and the chunks after it) are clamped to T - 1:
-    // the pre-pass gives those tokens beta 0 and alpha 1, and their k only
-    // meets a zero coefficient.
+    // formed once; a chunk then adds a uniform offset per row.  Rows past T
+    // (the tail chunk and the chunks after it) are not read: their loads are
+    // predicated off and the registers zeroed (the pre-pass gives those tokens
+    // beta 0 and alpha 1, so their k, q and v only meet zero coefficients).
     const int tl = tid >> 5;
     const float *kb = a.k + (row_base + tl) * a.qk_stride + (int64_t)kh * kD + (tid & 31) * 4;
     const float *qb = a.q + (kb - a.k);
     f32x4 pk[2], pq[2];   // vector-typed so they stay in registers
     auto prefetch_kq = [&](int c) {
         const int t0 = c * kC;
-        if (t0 + kC <= T) {
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int64_t off = (int64_t)(t0 + 8 * u) * a.qk_stride;
-                pk[u] = *reinterpret_cast<const f32x4 *>(kb + off);
-                pq[u] = *reinterpret_cast<const f32x4 *>(qb + off);
-            }
-        } else {
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int t = t0 + tl + 8 * u < T ? t0 + 8 * u : T - 1 - tl;
-                const int64_t off = (int64_t)t * a.qk_stride;
+        for (int u = 0; u < 2; ++u) {
+            const int64_t off = (int64_t)(t0 + 8 * u) * a.qk_stride;   // uniform
+            pk[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            pq[u] = pk[u];
+            if (t0 + tl + 8 * u < T) {
                 pk[u] = *reinterpret_cast<const f32x4 *>(kb + off);
                 pq[u] = *reinterpret_cast<const f32x4 *>(qb + off);
             }
@@ -285,19 +279,17 @@ __global__ void __launch_bounds__(256) split_kernel(StepArgs a, const float *ws,
     float vv[4];
     f32x4 Tr, Gr, Br, Pr, Dr;
     float Plast;
+    // Only half 0 uses v (predicated loads; rows past T read nothing and give 0).
+    // Both halves load the whole record: loading T in one half and G in the
+    // other made the compiler keep the pair in scratch.
     auto load_chunk = [&](int c) {
         const int t0 = c * kC;
-        if (t0 + kC <= T) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) vv[r] = vb[(int64_t)(t0 + r) * a.v_stride];
-        } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = t0 + 4 * g + r < T ? t0 + r : T - 1 - 4 * g;
-                vv[r] = vb[(int64_t)t * a.v_stride];
-            }
-        }
         const float *rec = wsh + (int64_t)(c < nc ? c : nc - 1) * kSeqRec;   // uniform
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            vv[r] = 0.0f;
+            if (half == 0 && t0 + 4 * g + r < T) vv[r] = vb[(int64_t)(t0 + r) * a.v_stride];
+        }
         Tr = *reinterpret_cast<const f32x4 *>(rec + lrec);
         Gr = *reinterpret_cast<const f32x4 *>(rec + 256 + lrec);
         Br = *reinterpret_cast<const f32x4 *>(rec + 512 + 4 * g);
@@ -350,10 +342,6 @@ __global__ void __launch_bounds__(256) split_kernel(StepArgs a, const float *ws,
         f32x4 Cp, O;
         if (half == 0) {
             const f32x4 U = Up + x_s[w ^ 1][0][l];
-            if (nt < kC) {   // tail chunk: tokens past T read a clamped row
-#pragma unroll
-                for (int r = 0; r < 4; ++r) vv[r] = 4 * g + r < nt ? vv[r] : 0.0f;
-            }
             f32x4 R;
 #pragma unroll
             for (int r = 0; r < 4; ++r) R[r] = Br[r] * (vv[r] - Pr[r] * gam * U[r]);
