@@ -682,6 +682,35 @@ def test_graph_replay_matches_eager(g):
             assert torch.equal(st_g[l], st_e[l]), (rep, l)
 
 
+def test_sequence_workspace_shared_and_odd_heads(g):
+    """The workspace entry at one value head per key head and 15 heads (the
+    workgroup mapping's partial group of eight), twice in a row on one shared
+    workspace with different inputs, and the size check (a workspace one byte
+    short is rejected before any launch, leaving the state untouched)."""
+    import torch
+    B, NK, NV, D = 3, 5, 5, 128
+    ws = torch.empty(g.gdn_seq_workspace_bytes(B, 40, NV, D), dtype=torch.uint8, device="cuda:0")
+    for T, seed in ((40, 1501), (23, 1502)):      # the second call leaves part of the workspace stale
+        c = inputs.make_case(seed, B=B, NK=NK, NV=NV, D=D, T=T)
+        say("seq workspace shared", T)
+        d = _dev_case(c)
+        st = dev(c.state)
+        o = g.gdn_recurrence_seq_ws(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                                    workspace=ws, seq_len=T, num_k_heads=NK, num_v_heads=NV,
+                                    head_dim=D)
+        ref_st = c.state.copy()
+        ref = orc.seq(ref_st, c.q, c.k, c.v, c.alpha, c.beta, B=B, T=T, NK=NK, NV=NV, Dk=D, Dv=D)
+        assert out_err(host(o), ref, NV, D) < TOL_CHAIN, T
+        assert tile_err(host(st), ref_st, NV, D) < TOL_CHAIN, T
+    need = g.gdn_seq_workspace_bytes(B, 23, NV, D)
+    before = host(st).copy()
+    with pytest.raises(g.GdnError):
+        g.gdn_recurrence_seq_ws(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                                workspace=ws[:need - 1], seq_len=23, num_k_heads=NK,
+                                num_v_heads=NV, head_dim=D)
+    assert np.array_equal(host(st), before)
+
+
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("T", [1, 15, 16, 17, 32, 33, 48])
 @pytest.mark.parametrize("norm", [False, True])
