@@ -61,7 +61,10 @@ __device__ __forceinline__ float dpp_from_above(float x) {
 // straight from global memory into the matrix-core operand layout (lane (g, li)
 // holds row li, columns 16m + 4g .. +3), and the alpha, beta loads of up to 16
 // value heads are issued together, ahead of the work on them.
-__global__ void __launch_bounds__(64) prep_kernel(StepArgs a, float *ws, int nc) {
+// Four waves per SIMD (122 VGPRs, no spill; five or more spill): the pre-pass
+// is bound by its own traffic, so more waves in flight help.
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) prep_kernel(StepArgs a, float *ws,
+                                                                                           int nc) {
     constexpr int kHG = 16;   // value heads whose alpha, beta are staged at once
     __shared__ __align__(16) float m_s[kC * kTS];   // M[t][s]
     __shared__ __align__(16) float a_s[kC * kTS];   // a_s[s][t] = A[t][s]
