@@ -21,12 +21,13 @@
 // head (32 state rows).  Wave (strip, half) owns rows 16 strip .. +15 of the
 // quarter and key columns 64 half .. +63: four 16x16 accumulator tiles.  The
 // two halves of a strip form partial U = S0 K^T and W = S0 Q^T over their
-// columns and exchange them through LDS, then both run the chain for their
-// strip and update their own columns.  192 heads make 768 workgroups, three per
-// CU and three waves per SIMD on all 256 CUs, each wave issuing 56 matrix-core
-// products per chunk (a workgroup per head puts two 104-product waves on each
-// SIMD of 192 CUs).  Waves of different workgroups share a SIMD, so one
-// workgroup's barrier and chain latency are covered by the others' products.
+// columns and exchange them through LDS; half 0 then forms C', half 1 O from
+// it, and both update their own columns.  192 heads make 768 workgroups, three
+// per CU and three waves per SIMD on all 256 CUs, each wave issuing 52
+// matrix-core products per chunk (a workgroup per head puts two 104-product
+// waves on each SIMD of 192 CUs).  Waves of different workgroups share a SIMD,
+// so one workgroup's barrier and chain latency are covered by the others'
+// products.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
