@@ -266,6 +266,50 @@ def run_norm_q(g, calls: int, pools: int = 16):
             "hbm_frac_algorithmic": round(algo / ms / 1e6 / HBM_PEAK_GBS, 4)}
 
 
+def run_strided(g, calls: int, pools: int = 16):
+    """The decode workload on packed projection rows: q | k | v read as column
+    slices of one [B, 10240] row (2048 + 2048 + 6144 floats), z at an offset in a
+    [B, 16384] row, alpha and beta interleaved in one [B, 96] row, rotated over
+    state pools.  The kernel is the same; only the strides differ."""
+    import torch
+    from gated_deltanet_decode_delta_amd import inputs
+
+    c = inputs.config_case("batched")
+    B, NK, NV, D = c.B, c.NK, c.NV, c.D
+    dev = "cuda:0"
+    log(f"[bench] strided rows: B={B} pools={pools}")
+    st0 = torch.from_numpy(c.state).to(dev)
+    states = [st0.clone() for _ in range(pools)]
+    del st0
+    qkv = torch.empty((B, 10240), dtype=torch.float32, device=dev)
+    qkv[:, :NK * D] = torch.from_numpy(c.q).to(dev)
+    qkv[:, NK * D:2 * NK * D] = torch.from_numpy(c.k).to(dev)
+    qkv[:, 2 * NK * D:] = torch.from_numpy(c.v).to(dev)
+    zrow = torch.zeros((B, 16384), dtype=torch.float32, device=dev)
+    zrow[:, 8192:8192 + NV * D] = torch.from_numpy(c.z).to(dev)
+    ab = torch.empty((B, 2 * NV), dtype=torch.float32, device=dev)
+    ab[:, :NV] = torch.from_numpy(c.alpha).to(dev)
+    ab[:, NV:] = torch.from_numpy(c.beta).to(dev)
+    gn = torch.from_numpy(c.gn).to(dev)
+    out = torch.empty((B, NV * D), dtype=torch.float32, device=dev)
+    q, k, v = qkv[:, :NK * D], qkv[:, NK * D:2 * NK * D], qkv[:, 2 * NK * D:]
+    z, al, be = zrow[:, 8192:8192 + NV * D], ab[:, :NV], ab[:, NV:]
+
+    def step(i):
+        g.gdn_decode_norm(states[i % pools], q, k, v, al, be, z, gn, c.eps, out=out,
+                          num_k_heads=NK, num_v_heads=NV)
+
+    ms = _timed(step, calls, 5)
+    algo = B * NV * head_bytes(D, NV, NK, 4, 4, True)
+    del states, qkv, zrow, ab, out
+    torch.cuda.empty_cache()
+    return {"workload": "batched decode with fused norm on packed rows (q|k|v in [64,10240], z in "
+                        "[64,16384]), B=64, NV=48, NK=16, D=128, padded pool",
+            "ms_per_call": round(ms, 5),
+            "state_GBps": round(2.0 * B * NV * D * D * 4 / ms / 1e6, 1),
+            "hbm_frac_algorithmic": round(algo / ms / 1e6 / HBM_PEAK_GBS, 4)}
+
+
 def run_fused(g, calls: int, pools: int = 16):
     """The decode workload with the input stage fused in front (4-tap conv ring,
     silu, L2 of q/k, gates): one launch per layer from the projection row, with
@@ -559,7 +603,7 @@ def main():
     ap.add_argument("--pools", type=int, default=48)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-extra", action="store_true", help="main workload only")
-    ap.add_argument("--extras", default="fp16_state,sequence,verify,norm_q,fused,real_head",
+    ap.add_argument("--extras", default="fp16_state,sequence,verify,norm_q,strided,fused,real_head",
                     help="comma list of extra workloads: fp16_state, sequence, verify, norm_q, "
                          "fused, real_head")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -608,7 +652,7 @@ def main():
     wanted = [] if args.no_extra else [w for w in args.extras.split(",") if w]
     runners = {"fp16_state": lambda: run_fp16(g, 100), "sequence": lambda: run_seq(g, 20),
                "verify": lambda: run_verify(g, 100), "norm_q": lambda: run_norm_q(g, 200),
-               "fused": lambda: run_fused(g, 200),
+               "strided": lambda: run_strided(g, 200), "fused": lambda: run_fused(g, 200),
                "real_head": lambda: run_real_head(g, 50)}
     for w in wanted:
         extra[w] = runners[w]()
