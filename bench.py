@@ -153,7 +153,7 @@ def run_seq(g, calls: int):
     B, T, NK, NV, D = c.B, c.T, c.NK, c.NV, c.D
     dev = "cuda:0"
     log(f"[bench] sequence: B={B} T={T}")
-    t = {n: torch.from_numpy(getattr(c, n)).to(dev) for n in ("q", "k", "v", "alpha", "beta")}
+    t = {n: torch.from_numpy(getattr(c, n)).to(dev) for n in ("q", "k", "v", "z", "alpha", "beta", "gn")}
     st = torch.from_numpy(c.state).to(dev)
     out = torch.empty((B * T, NV * D), dtype=torch.float32, device=dev)
 
@@ -170,8 +170,19 @@ def run_seq(g, calls: int):
 
     # the workspace path takes ~20 calls to settle (the first five run ~20%
     # slower on a fresh box), so both paths get 20 warmup calls
+    def step_norm(i):   # with z: the gated norm fused into the output
+        g.gdn_recurrence_seq_ws(st, t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["z"],
+                                t["gn"], c.eps, out=out, workspace=ws, seq_len=T,
+                                num_k_heads=NK, num_v_heads=NV)
+
+    def step_norm_plain(i):
+        g.gdn_recurrence_seq(st, t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["z"], t["gn"],
+                             c.eps, out=out, seq_len=T, num_k_heads=NK, num_v_heads=NV)
+
     ms = _timed(step, calls, 20)
     ms_plain = _timed(step_plain, calls, 20)
+    ms_norm = _timed(step_norm, calls, 5)
+    ms_norm_plain = _timed(step_norm_plain, calls, 5)
     flops = 7.0 * D * D * B * NV * T
     byts = B * T * (2 * NK * D * 4 + NV * (D * 4 + 8 + D * 4)) + 2.0 * B * NV * D * D * 4
     del t, st, out, ws
@@ -181,7 +192,9 @@ def run_seq(g, calls: int):
             "ms_per_call": round(ms, 4), "tflops": round(flops / ms / 1e9, 2),
             "fp32_matrix_frac": round(flops / ms / 1e9 / FP32_VALU_PEAK_TFLOPS, 4),
             "GBps": round(byts / ms / 1e6, 1), "tokens_per_s": round(B * T / ms * 1e3, 1),
-            "no_workspace_ms_per_call": round(ms_plain, 4)}
+            "no_workspace_ms_per_call": round(ms_plain, 4),
+            "z_fused_norm_ms_per_call": round(ms_norm, 4),
+            "z_fused_norm_no_workspace_ms_per_call": round(ms_norm_plain, 4)}
 
 
 def run_verify(g, calls: int, pools: int = 16):

@@ -315,14 +315,15 @@ gdn_status gdn_recurrence_seq_ws(float *state, int64_t state_seq_stride, const f
     gdn_status s = validate(c, &empty, &sp);
     if (s != GDN_OK || empty) return s;
     gdn::StepArgs a = to_args(c, state, out);
-    if (norm || k_dim != 128)
+    if (k_dim != 128)
         return finish(gdn::launch_seq(a, k_dim, norm ? gdn::kOutNormF32 : gdn::kOutRawF32,
                                       (hipStream_t)stream));
     const int64_t need = gdn_seq_workspace_bytes(batch, seq_len, num_v_heads, k_dim, v_dim);
     if (need < 0) return GDN_ERR_SHAPE;
     // one pre-pass workgroup per (sequence, key head, chunk), four per value head
     if ((int64_t)batch * num_k_heads * ((seq_len + 15) / 16) > INT32_MAX ||
-        (int64_t)batch * num_v_heads * 4 > INT32_MAX)
+        (int64_t)batch * num_v_heads * 4 > INT32_MAX ||
+        ((int64_t)batch * seq_len * num_v_heads + 15) / 16 > INT32_MAX)
         return GDN_ERR_SHAPE;
     if (!workspace) return GDN_ERR_NULL;
     if (workspace_bytes < need) return GDN_ERR_ARG;

@@ -71,8 +71,8 @@ hipError_t launch_seq_mfma(const StepArgs &a, OutMode mode, hipStream_t stream);
 // Floats of one workspace record of the split sequence path: one per (sequence,
 // value head, 16-token chunk) -- T and G (16x16 each, row-major), beta, P and D.
 constexpr int kSeqRec = 576;
-// dim 128, raw output: chunk pre-pass into ws, then the state pass (four
-// workgroups per head)
+// dim 128: chunk pre-pass into ws, then the state pass (four workgroups per
+// head) writing raw o; with a.z set, then the gated norm over the output rows
 hipError_t launch_seq_split(const StepArgs &a, float *ws, hipStream_t stream);
 hipError_t launch_f32_to_f16(const float *src, uint16_t *dst, int64_t n, hipStream_t stream);
 hipError_t launch_f16_to_f32(const uint16_t *src, float *dst, int64_t n, hipStream_t stream);

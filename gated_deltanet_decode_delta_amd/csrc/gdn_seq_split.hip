@@ -409,6 +409,40 @@ __global__ void __launch_bounds__(256) split_kernel(StepArgs a, const float *ws,
     for (int m = 0; m < 4; ++m) *reinterpret_cast<f32x4 *>(srow + 16 * m) = S[m] * gam;
 }
 
+// ---------------------------------------------------------------------------
+// Gated RMS norm over the output rows, in place (the state pass writes raw o;
+// four workgroups per head cannot form a head's sum of o^2 between them).
+// logicaffeine "codegen_cuda/gdn.rs" `gdn_gate_norm`: r = sqrt(mean_i o_i^2 + eps),
+// y_i = gn_i o_i / r * z_i sigmoid(z_i).  Sixteen lanes per (row, head), eight
+// values each; the sum is a DPP reduction within the sixteen.
+__global__ void __launch_bounds__(256) norm_rows_kernel(StepArgs a, int64_t items) {
+    const int64_t item = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);   // (row, head)
+    if (item >= items) return;   // whole sixteen-lane groups leave together
+    const int j = threadIdx.x & 15;
+    const int64_t row = item / a.nv;
+    const int h = (int)(item - row * a.nv);
+    float *o = static_cast<float *>(a.out) + row * a.out_stride + (int64_t)h * kD + 8 * j;
+    const float *z = a.z + row * a.z_stride + (int64_t)h * kD + 8 * j;
+    const f32x4 o0 = *reinterpret_cast<const f32x4 *>(o), o1 = *reinterpret_cast<const f32x4 *>(o + 4);
+    const f32x4 z0 = *reinterpret_cast<const f32x4 *>(z), z1 = *reinterpret_cast<const f32x4 *>(z + 4);
+    // the norm weight needs only 4-byte alignment: scalar loads (it stays in cache)
+    const float *gp = a.gn + 8 * j;
+    const f32x4 g0 = f32x4{gp[0], gp[1], gp[2], gp[3]}, g1 = f32x4{gp[4], gp[5], gp[6], gp[7]};
+    float ss = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ss += o0[e] * o0[e] + o1[e] * o1[e];
+    ss = group_sum<16>(ss);
+    const float r = sqrtf(ss * (1.0f / kD) + a.eps);
+    f32x4 y0, y1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        y0[e] = (g0[e] * o0[e] / r) * silu(z0[e]);
+        y1[e] = (g1[e] * o1[e] / r) * silu(z1[e]);
+    }
+    *reinterpret_cast<f32x4 *>(o) = y0;
+    *reinterpret_cast<f32x4 *>(o + 4) = y1;
+}
+
 hipError_t launch_seq_split(const StepArgs &a, float *ws, hipStream_t stream) {
     const int nc = (a.seq_len + kC - 1) / kC;
     const int64_t items = (int64_t)a.batch * a.nk * nc;
@@ -417,6 +451,11 @@ hipError_t launch_seq_split(const StepArgs &a, float *ws, hipStream_t stream) {
     if (e != hipSuccess) return e;
     const unsigned grid = (unsigned)((int64_t)a.batch * a.nv * 4);
     hipLaunchKernelGGL(split_kernel, dim3(grid), dim3(256), 0, stream, a, (const float *)ws, nc);
+    e = hipGetLastError();
+    if (e != hipSuccess || a.z == nullptr) return e;
+    const int64_t rows = (int64_t)a.batch * a.seq_len * a.nv;   // (row, head) pairs
+    hipLaunchKernelGGL(norm_rows_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, a,
+                       rows);
     return hipGetLastError();
 }
 

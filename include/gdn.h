@@ -187,14 +187,14 @@ gdn_status gdn_recurrence_seq(float *state, int64_t state_seq_stride,
 /*
  * gdn_recurrence_seq_ws -- gdn_recurrence_seq with a caller-provided device
  * workspace.  Same operation, arguments, layouts and results (within the fp32
- * tolerance; the summation order differs).  For k_dim == v_dim == 128 and the
- * raw output (z == NULL) it runs in two launches: a pre-pass forms, for every
- * (sequence, value head, 16-token chunk), the input-only quantities of the
- * chunked form of the recurrence (the inverse of the chunk's unit lower
- * triangular system, the decayed k.q matrix, beta and the decay products) into
- * the workspace, and the state pass then splits each head over four
- * workgroups.  Any other call ignores the workspace (it may be NULL) and runs
- * as gdn_recurrence_seq.  Source: metrale ssm_gdn_a.rs, launcher
+ * tolerance; the summation order differs).  For k_dim == v_dim == 128 it runs
+ * in two launches: a pre-pass forms, for every (sequence, value head, 16-token
+ * chunk), the input-only quantities of the chunked form of the recurrence (the
+ * inverse of the chunk's unit lower triangular system, the decayed k.q matrix,
+ * beta and the decay products) into the workspace, and the state pass then
+ * splits each head over four workgroups and writes the raw o.  With z, a third
+ * launch applies the gated norm to the output rows in place.  Any other head
+ * dim ignores the workspace (it may be NULL) and runs as gdn_recurrence_seq.  Source: metrale ssm_gdn_a.rs, launcher
  * `gdn_prefill_regresident` (the operation); the chunked form is exact algebra
  * on logicaffeine gdn.rs `gdn_step`.
  *   workspace        device memory of at least gdn_seq_workspace_bytes(...)

@@ -272,7 +272,31 @@ def test_sequence_4096_tokens(g, seq, init):
         assert tile_err(got_s[b:b + 1, sl], ref_state[b:b + 1, sl], 1, D) < TOL_CHAIN, (b, h)
 
 
-def test_sequence_fused_norm_ragged(g):
+def test_sequence_4096_tokens_fused_norm(g, seq):
+    """The full sequence workload with z (the gated norm fused into the output):
+    sampled heads through 4096 oracle steps, every token's y and the final state."""
+    c = inputs.config_case("sequence")
+    B, T, NK, NV, D = c.B, c.T, c.NK, c.NV, c.D
+    say("sequence norm", B, T)
+    d = _dev_case(c)
+    st = dev(c.state)
+    y = seq(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["z"], d["gn"], c.eps,
+            seq_len=T, num_k_heads=NK, num_v_heads=NV)
+    heads = _sample_heads(B, NV, 6, 57)
+    ref_state = c.state.copy()
+    ref = orc.seq_head_threaded(ref_state, c.q, c.k, c.v, c.alpha, c.beta, B=B, T=T, NK=NK,
+                                NV=NV, Dk=D, Dv=D, heads=heads, threads=6, z=c.z, gn=c.gn,
+                                eps=c.eps)
+    got_y, got_s = host(y), host(st)
+    for (b, h) in heads:
+        rows = slice(b * T, (b + 1) * T)
+        osl = slice(h * D, (h + 1) * D)
+        assert out_err(got_y[rows, osl], ref[rows, osl], 1, D) < TOL_CHAIN, (b, h)
+        sl = slice(h * D * D, (h + 1) * D * D)
+        assert tile_err(got_s[b:b + 1, sl], ref_state[b:b + 1, sl], 1, D) < TOL_CHAIN, (b, h)
+
+
+def test_sequence_fused_norm_ragged(g, seq):
     """Sequence kernel with z (fused gated norm), a length that is not a multiple
     of the staging chunk, every head."""
     B, T, NK, NV, D = 2, 37, 16, 48, 128
@@ -280,8 +304,8 @@ def test_sequence_fused_norm_ragged(g):
     say("sequence norm ragged T=37")
     d = _dev_case(c)
     st = dev(c.state)
-    y = g.gdn_recurrence_seq(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["z"], d["gn"],
-                             c.eps, seq_len=T, num_k_heads=NK, num_v_heads=NV)
+    y = seq(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["z"], d["gn"],
+            c.eps, seq_len=T, num_k_heads=NK, num_v_heads=NV)
     ref_state = c.state.copy()
     ref = orc.seq(ref_state, c.q, c.k, c.v, c.alpha, c.beta, B=B, T=T, NK=NK, NV=NV, Dk=D, Dv=D,
                   z=c.z, gn=c.gn, eps=c.eps)
