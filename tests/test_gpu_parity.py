@@ -494,7 +494,27 @@ def test_deterministic_bitwise(g):
     assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
 
 
-@pytest.mark.parametrize("kind", ["decode", "f16", "seq128", "seq64"])
+def test_sequence_workspace_deterministic_bitwise(g):
+    """The workspace sequence path twice on the same inputs (a fresh workspace
+    each time, the first filled with NaN): the same bits, outputs and states."""
+    import torch
+    B, T, NK, NV, D = 4, 70, 16, 48, 128
+    c = inputs.make_case(64, B=B, NK=NK, NV=NV, D=D, T=T)
+    say("determinism, workspace sequence")
+    d = _dev_case(c)
+    outs = []
+    for fill in (float("nan"), 0.0):
+        ws = torch.full((g.gdn_seq_workspace_bytes(B, T, NV, D) // 4,), fill,
+                        dtype=torch.float32, device="cuda:0")
+        st = dev(c.state)
+        o = g.gdn_recurrence_seq_ws(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                                    workspace=ws.view(torch.uint8), seq_len=T, num_k_heads=NK,
+                                    num_v_heads=NV, head_dim=D)
+        outs.append((host(st).view(np.uint32), host(o).view(np.uint32)))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+
+
+@pytest.mark.parametrize("kind", ["decode", "f16", "seq128", "seq64", "seq128ws", "seq128ws_norm"])
 def test_batch_permutation_permutes_results_bitwise(g, kind):
     """Sequences are independent: running a permuted batch gives the permuted
     outputs and states bit for bit (a wide launch for every kernel family)."""
@@ -521,6 +541,12 @@ def test_batch_permutation_permutes_results_bitwise(g, kind):
                                       dev(c.gn), c.eps, out_dtype=torch.bfloat16, num_k_heads=NK,
                                       num_v_heads=NV)
             return host(y), host(st16)
+        if kind.startswith("seq128ws"):   # pre-pass, four workgroups per head (and the norm pass)
+            zkw = dict(z=d["z"], norm_weight=dev(c.gn), eps=c.eps) if kind.endswith("norm") else {}
+            o = g.gdn_recurrence_seq_ws(st32, d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                                        seq_len=T, num_k_heads=NK, num_v_heads=NV, head_dim=D,
+                                        **zkw)
+            return host(o), host(st32).view(np.uint32)
         o = g.gdn_recurrence_seq(st32, d["q"], d["k"], d["v"], d["alpha"], d["beta"], seq_len=T,
                                  num_k_heads=NK, num_v_heads=NV, head_dim=D)
         return host(o), host(st32).view(np.uint32)
