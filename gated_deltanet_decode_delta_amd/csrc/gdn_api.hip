@@ -315,16 +315,17 @@ gdn_status gdn_recurrence_seq_ws(float *state, int64_t state_seq_stride, const f
     gdn_status s = validate(c, &empty, &sp);
     if (s != GDN_OK || empty) return s;
     gdn::StepArgs a = to_args(c, state, out);
-    if (k_dim != 128)
+    // The split path launches one pre-pass workgroup per (sequence, key head,
+    // chunk), four state-pass workgroups per value head and one norm workgroup
+    // per 16 (row, head) pairs; a shape whose grids would not fit 32 bits, or
+    // another head dim, runs the kernels without a workspace.
+    if (k_dim != 128 || (int64_t)batch * num_k_heads * ((seq_len + 15) / 16) > INT32_MAX ||
+        (int64_t)batch * num_v_heads * 4 > INT32_MAX ||
+        ((int64_t)batch * seq_len * num_v_heads + 15) / 16 > INT32_MAX)
         return finish(gdn::launch_seq(a, k_dim, norm ? gdn::kOutNormF32 : gdn::kOutRawF32,
                                       (hipStream_t)stream));
     const int64_t need = gdn_seq_workspace_bytes(batch, seq_len, num_v_heads, k_dim, v_dim);
     if (need < 0) return GDN_ERR_SHAPE;
-    // one pre-pass workgroup per (sequence, key head, chunk), four per value head
-    if ((int64_t)batch * num_k_heads * ((seq_len + 15) / 16) > INT32_MAX ||
-        (int64_t)batch * num_v_heads * 4 > INT32_MAX ||
-        ((int64_t)batch * seq_len * num_v_heads + 15) / 16 > INT32_MAX)
-        return GDN_ERR_SHAPE;
     if (!workspace) return GDN_ERR_NULL;
     if (workspace_bytes < need) return GDN_ERR_ARG;
     Span ws;
