@@ -74,6 +74,8 @@ constexpr int kSeqRec = 576;
 // dim 128: chunk pre-pass into ws, then the state pass (four workgroups per
 // head) writing raw o; with a.z set, then the gated norm over the output rows
 hipError_t launch_seq_split(const StepArgs &a, float *ws, hipStream_t stream);
+// the gated norm over T-token output rows in place (a.out raw o, a.z, a.gn; dim 128)
+hipError_t launch_norm_rows(const StepArgs &a, hipStream_t stream);
 hipError_t launch_f32_to_f16(const float *src, uint16_t *dst, int64_t n, hipStream_t stream);
 hipError_t launch_f16_to_f32(const uint16_t *src, float *dst, int64_t n, hipStream_t stream);
 

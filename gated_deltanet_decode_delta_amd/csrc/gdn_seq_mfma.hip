@@ -31,8 +31,9 @@
 // of the state work: during chunk c, chunk c+2 is staged and its k.k / k.q tiles
 // and range products formed, and the triangular inverse of chunk c+1 is
 // solved, so the first half of every chunk is the U / W products alone, equal
-// on every SIMD; two workgroup barriers per chunk.  v and z go from global
-// memory straight to the lanes that use them.
+// on every SIMD; two workgroup barriers per chunk.  v goes from global memory
+// straight to the lanes that use it.  The kernel writes the raw o; with z the
+// gated norm follows as a second pass over the output rows.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -69,7 +70,6 @@ __device__ __forceinline__ float dpp_from_above(float x) {
 
 }  // namespace
 
-template <bool NORM>
 __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
     // Chunk data: buffer c % 3 holds chunk c's k, q, alpha, beta, P and D
     // (chunks c, c+1, c+2 are live during chunk c); the k.k / k.q partials, M,
@@ -80,7 +80,6 @@ __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
     __shared__ __align__(16) float a_s[kC * kTS], t_s[2][kC * kTS];  // A and T = (I + A)^{-1}
     __shared__ __align__(16) float m_s[2][kC * kTS], mt_s[2][kC * kTS]; // M[t][s] and its transpose
     __shared__ __align__(16) float al_s[kBufs][kC], be_s[kBufs][kC], p_s[kBufs][kC], d_s[kBufs][kC];
-    __shared__ float nrm_s[NORM ? kWaves : 1][kC];
 
     const int tid = threadIdx.x;
     const int w = tid >> 6, l = tid & 63, g = l >> 4, li = l & 15;
@@ -102,16 +101,15 @@ __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
     for (int m = 0; m < 8; ++m)
         S[m] = *reinterpret_cast<const f32x4 *>(slot + (int64_t)row * kD + 16 * m + 4 * g);
     float gam = 1.0f;
-    const float gnv = NORM ? a.gn[row] : 0.0f;
 
     // prefetch registers for one chunk: 16-byte pieces f = tid + 256u of the
     // chunk's k and q ([16][128]); v (and z) of the lane's own (t, i) entries
     float4 pk[kPieces], pq[kPieces];
-    float pv[4], pz[4];
+    float pv[4];
     float pal = 1.0f, pbe = 0.0f;
     // element offsets of this lane's prefetch rows at t0 = 0: k/q piece u is
-    // token f >> 5, columns (f & 31) * 4 .. +3 (f = tid + 512u); v and z are the
-    // lane's column of tokens 4g .. 4g + 3
+    // token f >> 5, columns (f & 31) * 4 .. +3 (f = tid + 512u); v is the lane's
+    // column of tokens 4g .. 4g + 3
     int64_t kq_off[kPieces];
 #pragma unroll
     for (int u = 0; u < kPieces; ++u) {
@@ -119,7 +117,6 @@ __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
         kq_off[u] = (row_base + (f >> 5)) * a.qk_stride + (int64_t)kh * kD + (f & 31) * 4;
     }
     const int64_t v_off = (row_base + 4 * g) * a.v_stride + vcol;
-    const int64_t z_off = NORM ? (row_base + 4 * g) * a.z_stride + vcol : 0;
     auto prefetch = [&](int t0) {
         if (t0 + kC <= T) {   // a whole chunk: uniform row offsets, nothing to clamp
             const int64_t dqk = (int64_t)t0 * a.qk_stride;
@@ -131,7 +128,6 @@ __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 pv[r] = a.v[v_off + (int64_t)(t0 + r) * a.v_stride];
-                pz[r] = NORM ? a.z[z_off + (int64_t)(t0 + r) * a.z_stride] : 0.f;
             }
             {   // every lane loads (token tid % 16): no divergent branch among the loads
                 const int64_t rr = row_base + t0 + (tid & (kC - 1));
@@ -163,12 +159,6 @@ __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
             const int64_t rr = row_base + (ok ? t0 + t : T - 1);
             const float vx = a.v[rr * a.v_stride + vcol];
             pv[r] = ok ? vx : 0.f;
-            if constexpr (NORM) {
-                const float zx = a.z[rr * a.z_stride + vcol];
-                pz[r] = ok ? zx : 0.f;
-            } else {
-                pz[r] = 0.f;
-            }
         }
         pal = 1.0f;
         pbe = 0.0f;
@@ -293,19 +283,16 @@ __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
         }
     };
 
-    float vcur[4], zcur[4], vn1[4], zn1[4], vn2[4], zn2[4];
-    auto take = [&](float *vd, float *zd) {
+    float vcur[4], vn1[4], vn2[4];
+    auto take = [&](float *vd) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            vd[r] = pv[r];
-            zd[r] = pz[r];
-        }
+        for (int r = 0; r < 4; ++r) vd[r] = pv[r];
     };
     // Prologue: chunk 0 staged and prepared, chunk 1 staged and prepared, T of
     // chunk 0 solved, chunk 2's loads in flight.
     prefetch(0);
     stage(0);
-    take(vcur, zcur);
+    take(vcur);
     // drain every load (the state included) so that no conservative vmcnt wait
     // lands inside the chunk loop, where it would also wait for the prefetch
     __builtin_amdgcn_s_waitcnt(0);
@@ -314,7 +301,7 @@ __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
     partials(0, 0);
     if (kC < T) {
         stage(1);
-        take(vn1, zn1);
+        take(vn1);
     }
     __syncthreads();
     if (2 * kC < T) prefetch(2 * kC);
@@ -366,7 +353,7 @@ __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
         const f32x4 U = Ua + Ub, W = Wa + Wb;
         if (t0 + 2 * kC < T) {
             stage(b3n2);
-            take(vn2, zn2);
+            take(vn2);
         }
         __syncthreads();   // chunk c+2 staged
         if (t0 + 2 * kC < T) range_products(b3n2, par);   // waves 4..7, ahead of their state work
@@ -399,33 +386,11 @@ __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
             o1 = mfma(Ga[3], Cp[3], o1);
             O += o1;
         }
-        if constexpr (!NORM) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 4 * g + r;
-                // a whole chunk stores without per-token branches
-                if (nt == kC || t < nt) outp[(row_base + t0 + t) * a.out_stride + vcol] = O[r] * a.scale;
-            }
-        } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float o = O[r] * a.scale;
-                const float ss = group_sum<16>(o * o);
-                if (li == 0) nrm_s[w][4 * g + r] = ss;
-            }
-            __syncthreads();   // per-wave sums of o^2 visible
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 4 * g + r;
-                float tot = 0.f;
-#pragma unroll
-                for (int v2 = 0; v2 < kWaves; ++v2) tot += nrm_s[v2][t];
-                const float rr_ = sqrtf(tot * (1.0f / kD) + a.eps);
-                if (nt == kC || t < nt) {
-                    const float o = O[r] * a.scale;
-                    outp[(row_base + t0 + t) * a.out_stride + vcol] = (gnv * o / rr_) * silu(zcur[r]);
-                }
-            }
+        for (int r = 0; r < 4; ++r) {
+            const int t = 4 * g + r;
+            // a whole chunk stores without per-token branches
+            if (nt == kC || t < nt) outp[(row_base + t0 + t) * a.out_stride + vcol] = O[r] * a.scale;
         }
 
         // true state: gam S -> P_15 gam S + K^T (C' diag(M[15][.]))^T.  Keep the
@@ -461,9 +426,7 @@ __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             vcur[r] = vn1[r];
-            zcur[r] = zn1[r];
             vn1[r] = vn2[r];
-            zn1[r] = zn2[r];
         }
     }
 
@@ -474,13 +437,13 @@ __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
 
 hipError_t launch_seq_mfma(const StepArgs &a, OutMode mode, hipStream_t stream) {
     const unsigned grid = (unsigned)((int64_t)a.batch * a.nv);
-    if (mode == kOutRawF32)
-        hipLaunchKernelGGL(seq_mfma_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, a);
-    else if (mode == kOutNormF32)
-        hipLaunchKernelGGL(seq_mfma_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, a);
-    else
-        return hipErrorInvalidValue;
-    return hipGetLastError();
+    if (mode != kOutRawF32 && mode != kOutNormF32) return hipErrorInvalidValue;
+    // with z the output rows get the gated norm in a second pass: fusing it here
+    // (a workgroup-wide sum per token) took 1.56 ms against 1.42 ms for the pair
+    hipLaunchKernelGGL(seq_mfma_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || mode == kOutRawF32) return e;
+    return launch_norm_rows(a, stream);
 }
 
 }  // namespace gdn

@@ -453,6 +453,10 @@ hipError_t launch_seq_split(const StepArgs &a, float *ws, hipStream_t stream) {
     hipLaunchKernelGGL(split_kernel, dim3(grid), dim3(256), 0, stream, a, (const float *)ws, nc);
     e = hipGetLastError();
     if (e != hipSuccess || a.z == nullptr) return e;
+    return launch_norm_rows(a, stream);
+}
+
+hipError_t launch_norm_rows(const StepArgs &a, hipStream_t stream) {
     const int64_t rows = (int64_t)a.batch * a.seq_len * a.nv;   // (row, head) pairs
     hipLaunchKernelGGL(norm_rows_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, a,
                        rows);
