@@ -344,6 +344,7 @@ __global__ void __launch_bounds__(256) split_kernel(StepArgs a, const float *ws,
         // half 1 forms O = P gam W + G C' and stores the four tokens.  Both
         // update their own columns with C'.
         f32x4 Cp, O;
+        __builtin_amdgcn_s_setprio(2);   // the strip's dependent chain ahead of other waves' products
         if (half == 0) {
             const f32x4 U = Up + x_s[w ^ 1][0][l];
             f32x4 R;
@@ -356,6 +357,7 @@ __global__ void __launch_bounds__(256) split_kernel(StepArgs a, const float *ws,
             c1 = mfma(Tr[3], R[3], c1);
             Cp = c0 + c1;
             c_s[strip][l] = Cp;
+            __builtin_amdgcn_s_setprio(0);
         } else {
             const f32x4 W = Wp + x_s[w ^ 1][1][l];
 #pragma unroll
@@ -373,6 +375,7 @@ __global__ void __launch_bounds__(256) split_kernel(StepArgs a, const float *ws,
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 if (nt == kC || 4 * g + r < nt) ob[(int64_t)(t0 + r) * a.out_stride] = O[r] * a.scale;
+            __builtin_amdgcn_s_setprio(0);
         }
 
         // gam S -> P_15 gam S + K^T (C' diag(D))^T, the decay kept in gam while
