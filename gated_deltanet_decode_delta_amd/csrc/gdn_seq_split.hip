@@ -317,6 +317,16 @@ __global__ void __launch_bounds__(256) split_kernel(StepArgs a, const float *ws,
         const int bb = c & 1;
         const int t0 = c * kC;
         const int nt = T - t0 < kC ? T - t0 : kC;
+        // the update's k operands (token 4g + s4, column 64 half + 16 m + li),
+        // requested now so that their LDS latency is long past at the update
+        float kcv[16];
+        {
+            const float *kc = &k_s[bb][4 * g * kKS + 64 * half + li];
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) kcv[4 * s4 + m] = kc[s4 * kKS + 16 * m];
+        }
         // partial U^T = K S^T and W^T = Q S^T over this wave's 64 columns
         f32x4 Ua = f32x4{0.f, 0.f, 0.f, 0.f}, Ub = Ua, Wa = Ua, Wb = Ua;
 #pragma unroll
@@ -397,11 +407,10 @@ __global__ void __launch_bounds__(256) split_kernel(StepArgs a, const float *ws,
         gam = gnew;
 #pragma unroll
         for (int r = 0; r < 4; ++r) Cp[r] *= Dr[r] * cscale;
-        const float *kc = &k_s[bb][4 * g * kKS + 64 * half + li];   // k of token 4g + s4, column 64 half + 16 m + li
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
-            for (int m = 0; m < 4; ++m) S[m] = mfma(kc[s4 * kKS + 16 * m], Cp[s4], S[m]);
+            for (int m = 0; m < 4; ++m) S[m] = mfma(kcv[4 * s4 + m], Cp[s4], S[m]);
 
         // loads for the next chunks go out after this chunk's stores
         prefetch_kq(c + 2);
