@@ -197,7 +197,8 @@ __global__ void __launch_bounds__(kThreads) seq_mfma_kernel(StepArgs a) {
         if (w >= kWaves - 4) {
             const int e = tid - (kWaves - 4) * 64;   // 0 .. 255
             const int t = e >> 4, s = e & 15;
-            float m = s < t ? al_s[b3][s + 1] : 1.0f;
+            float m = al_s[b3][s < t ? s + 1 : 0];   // index kept inside the row
+        m = s < t ? m : 1.0f;
             m *= dpp_from_above<1>(m);
             m *= dpp_from_above<2>(m);
             m *= dpp_from_above<4>(m);

@@ -70,7 +70,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) pr
     __shared__ __align__(16) float m_s[kC * kTS];   // M[t][s]
     __shared__ __align__(16) float a_s[kC * kTS];   // a_s[s][t] = A[t][s]
     __shared__ __align__(16) float t_s[kC * kTS];   // T[t][s]
-    __shared__ float al_s[kHG][kC + 1], be_s[kHG][kC];
+    __shared__ float al_s[kHG][kC], be_s[kHG][kC];
 
     const int l = threadIdx.x, g = l >> 4, li = l & 15;
     const int item = blockIdx.x;
@@ -154,7 +154,8 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) pr
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 4 * g + r;
-                float x = li < t ? al_s[mm][li + 1] : 1.0f;
+                float x = al_s[mm][li < t ? li + 1 : 0];   // index kept to written entries
+                x = li < t ? x : 1.0f;
                 x *= dpp_from_above<1>(x);
                 x *= dpp_from_above<2>(x);
                 x *= dpp_from_above<4>(x);
