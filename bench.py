@@ -168,8 +168,8 @@ def run_seq(g, calls: int):
         g.gdn_recurrence_seq(st, t["q"], t["k"], t["v"], t["alpha"], t["beta"], out=out, seq_len=T,
                              num_k_heads=NK, num_v_heads=NV, head_dim=D)
 
-    # the workspace path takes ~20 calls to settle (the first five run ~20%
-    # slower on a fresh box), so both paths get 20 warmup calls
+    # after the chip has idled both paths run slower for their first tens of
+    # calls, so each gets 20 warmup calls
     def step_norm(i):   # with z: the gated norm fused into the output
         g.gdn_recurrence_seq_ws(st, t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["z"],
                                 t["gn"], c.eps, out=out, workspace=ws, seq_len=T,
