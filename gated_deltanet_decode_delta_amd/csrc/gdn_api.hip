@@ -5,6 +5,7 @@
 // one is wrong, so a rejected call leaves every buffer untouched.  Only then is
 // the kernel launched on the caller's stream.  No allocation, no
 // synchronisation, no printing.
+#include <algorithm>
 #include <math.h>
 #include <stdint.h>
 
@@ -317,11 +318,16 @@ gdn_status gdn_recurrence_seq_ws(float *state, int64_t state_seq_stride, const f
     gdn::StepArgs a = to_args(c, state, out);
     // The split path launches one pre-pass workgroup per (sequence, key head,
     // chunk), four state-pass workgroups per value head and one norm workgroup
-    // per 16 (row, head) pairs; a shape whose grids would not fit 32 bits, or
-    // another head dim, runs the kernels without a workspace.
+    // per 16 (row, head) pairs, and the state pass reads q, k, v and writes o
+    // through buffer descriptors with 32-bit offsets.  A shape whose grids
+    // would not fit 32 bits, whose rows of one sequence span 2^31 bytes or
+    // more in q, k, v or o, or another head dim, runs the kernels without a
+    // workspace.
+    const int64_t widest = std::max(a.qk_stride, std::max(a.v_stride, a.out_stride));
     if (k_dim != 128 || (int64_t)batch * num_k_heads * ((seq_len + 15) / 16) > INT32_MAX ||
         (int64_t)batch * num_v_heads * 4 > INT32_MAX ||
-        ((int64_t)batch * seq_len * num_v_heads + 15) / 16 > INT32_MAX)
+        ((int64_t)batch * seq_len * num_v_heads + 15) / 16 > INT32_MAX ||
+        (int64_t)seq_len * widest * 4 > INT32_MAX)
         return finish(gdn::launch_seq(a, k_dim, norm ? gdn::kOutNormF32 : gdn::kOutRawF32,
                                       (hipStream_t)stream));
     const int64_t need = gdn_seq_workspace_bytes(batch, seq_len, num_v_heads, k_dim, v_dim);

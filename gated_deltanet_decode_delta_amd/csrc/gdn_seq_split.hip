@@ -200,6 +200,27 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) pr
 }
 
 // ---------------------------------------------------------------------------
+// Raw buffer descriptors.  A descriptor covers nbytes from p (stride 0); the
+// hardware range check on the lane offset (offset + instruction offset) makes
+// a load at or past nbytes return 0 and drops a store there.  The state pass
+// moves each descriptor's base to the chunk's first row, so that the lane
+// offsets stay fixed over the loop and the rows past T need no predicate.
+// Callers keep every extent below 2^31 bytes.
+__device__ inline __amdgpu_buffer_rsrc_t buf_rsrc(const float *p, int64_t nbytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p), (short)0,
+                                             nbytes > 0 ? (int)nbytes : 0, 0x00020000);
+}
+__device__ inline f32x4 buf_load4(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ inline float buf_load1(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ inline void buf_store1(__amdgpu_buffer_rsrc_t r, int off, float x) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), r, off, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
 // State pass.  Block b_id -> (head, quarter): the four quarters of a head get
 // indices equal modulo 8, so they run on one XCD and share its L2 for the
 // head's workspace records and k, q rows.
@@ -236,7 +257,6 @@ __global__ void __launch_bounds__(256) split_kernel(StepArgs a, const float *ws,
     const int row = 32 * quarter + 16 * strip + li;          // state row (value index)
     float *srow = static_cast<float *>(a.state) + (int64_t)b * a.pitch + (int64_t)h * (kD * kD) +
                   (int64_t)row * kD + 64 * half + 4 * g;
-    const int64_t vcol = (int64_t)h * kD + row;
     const float *wsh = ws + (int64_t)head * nc * kSeqRec;
 
     // The true state is gam * S; S[m][r] = S[row][64 half + 16 m + 4 g + r].
@@ -246,26 +266,25 @@ __global__ void __launch_bounds__(256) split_kernel(StepArgs a, const float *ws,
     float gam = 1.0f;
 
     // k and q of a chunk: pieces f = tid + 256 u (u = 0, 1), token f >> 5 =
-    // tid / 32 + 8 u, columns (tid % 32) * 4.  Per-lane base pointers are
-    // formed once; a chunk then adds a uniform offset per row.  Rows past T
-    // (the tail chunk and the chunks after it) are not read: their loads are
-    // predicated off and the registers zeroed (the pre-pass gives those tokens
-    // beta 0 and alpha 1, so their k, q and v only meet zero coefficients).
+    // tid / 32 + 8 u, columns (tid % 32) * 4, read through descriptors based at
+    // the chunk's first row.  Rows past T (the tail chunk and the chunks after
+    // it) read 0 (the pre-pass gives those tokens beta 0 and alpha 1, so their
+    // k, q and v only meet zero coefficients).
     const int tl = tid >> 5;
-    const float *kb = a.k + (row_base + tl) * a.qk_stride + (int64_t)kh * kD + (tid & 31) * 4;
-    const float *qb = a.q + (kb - a.k);
+    const int64_t kq0 = row_base * a.qk_stride + (int64_t)kh * kD;
+    int kq_off[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) kq_off[u] = (int)(((tl + 8 * u) * a.qk_stride + (tid & 31) * 4) * 4);
     f32x4 pk[2], pq[2];   // vector-typed so they stay in registers
     auto prefetch_kq = [&](int c) {
         const int t0 = c * kC;
+        const int64_t off = kq0 + (int64_t)t0 * a.qk_stride;   // uniform
+        const int64_t nb = (int64_t)(T - t0) * a.qk_stride * 4;
+        const __amdgpu_buffer_rsrc_t rk = buf_rsrc(a.k + off, nb), rq = buf_rsrc(a.q + off, nb);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const int64_t off = (int64_t)(t0 + 8 * u) * a.qk_stride;   // uniform
-            pk[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-            pq[u] = pk[u];
-            if (t0 + tl + 8 * u < T) {
-                pk[u] = *reinterpret_cast<const f32x4 *>(kb + off);
-                pq[u] = *reinterpret_cast<const f32x4 *>(qb + off);
-            }
+            pk[u] = buf_load4(rk, kq_off[u]);
+            pq[u] = buf_load4(rq, kq_off[u]);
         }
     };
     auto stage = [&](int c) {
@@ -279,21 +298,25 @@ __global__ void __launch_bounds__(256) split_kernel(StepArgs a, const float *ws,
     };
     // per-chunk data of the lane: v of its row for tokens 4g .. 4g+3, and the
     // workspace record (T[li][4g..], G[li][4g..], beta, P, D at 4g.., P_15)
-    const float *vb = a.v + (row_base + 4 * g) * a.v_stride + vcol;
+    const int64_t v0 = row_base * a.v_stride + (int64_t)h * kD;
+    const int v_off = (int)((4 * g * a.v_stride + row) * 4);
+    const int v_step = (int)(a.v_stride * 4);
     const int lrec = li * kC + 4 * g;
     float vv[4];
     f32x4 Tr, Gr, Br, Pr, Dr;
     float Plast;
-    // Only half 0 uses v (predicated loads; rows past T read nothing and give 0).
-    // Both halves load the whole record: loading T in one half and G in the
-    // other made the compiler keep the pair in scratch.
+    // Only half 0 uses v (rows past T read 0).  Both halves load the whole
+    // record: loading T in one half and G in the other made the compiler keep
+    // the pair in scratch.
     auto load_chunk = [&](int c) {
         const int t0 = c * kC;
         const float *rec = wsh + (int64_t)(c < nc ? c : nc - 1) * kSeqRec;   // uniform
+        const __amdgpu_buffer_rsrc_t rv =
+            buf_rsrc(a.v + v0 + (int64_t)t0 * a.v_stride, (int64_t)(T - t0) * a.v_stride * 4);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             vv[r] = 0.0f;
-            if (half == 0 && t0 + 4 * g + r < T) vv[r] = vb[(int64_t)(t0 + r) * a.v_stride];
+            if (half == 0) vv[r] = buf_load1(rv, v_off + r * v_step);
         }
         Tr = *reinterpret_cast<const f32x4 *>(rec + lrec);
         Gr = *reinterpret_cast<const f32x4 *>(rec + 256 + lrec);
@@ -313,11 +336,13 @@ __global__ void __launch_bounds__(256) split_kernel(StepArgs a, const float *ws,
     load_chunk(0);
     __syncthreads();
 
-    float *ob = static_cast<float *>(a.out) + (row_base + 4 * g) * a.out_stride + vcol;
+    // o of the lane's row for tokens 4g .. 4g+3 (stores past T are dropped)
+    const float *o0 = static_cast<const float *>(a.out) + row_base * a.out_stride + (int64_t)h * kD;
+    const int o_off = (int)((4 * g * a.out_stride + row) * 4);
+    const int o_step = (int)(a.out_stride * 4);
     for (int c = 0; c < nc; ++c) {
         const int bb = c & 1;
         const int t0 = c * kC;
-        const int nt = T - t0 < kC ? T - t0 : kC;
         // the update's k operands (token 4g + s4, column 64 half + 16 m + li),
         // requested now so that their LDS latency is long past at the update
         float kcv[16];
@@ -383,9 +408,10 @@ __global__ void __launch_bounds__(256) split_kernel(StepArgs a, const float *ws,
             O = mfma(Gr[2], Cp[2], O);
             o1 = mfma(Gr[3], Cp[3], o1);
             O += o1;
+            const __amdgpu_buffer_rsrc_t ro =
+                buf_rsrc(o0 + (int64_t)t0 * a.out_stride, (int64_t)(T - t0) * a.out_stride * 4);
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (nt == kC || 4 * g + r < nt) ob[(int64_t)(t0 + r) * a.out_stride] = O[r] * a.scale;
+            for (int r = 0; r < 4; ++r) buf_store1(ro, o_off + r * o_step, O[r] * a.scale);
             __builtin_amdgcn_s_setprio(0);
         }
 

@@ -194,8 +194,9 @@ gdn_status gdn_recurrence_seq(float *state, int64_t state_seq_stride,
  * beta and the decay products) into the workspace, and the state pass then
  * splits each head over four workgroups and writes the raw o.  With z, a third
  * launch applies the gated norm to the output rows in place.  Any other head
- * dim, or a shape whose launch grids would exceed 2^31 workgroups, ignores the
- * workspace (it may be NULL) and runs as gdn_recurrence_seq.  Source: metrale ssm_gdn_a.rs, launcher
+ * dim, a shape whose launch grids would exceed 2^31 workgroups, or one where
+ * seq_len rows of q, k, v or out span 2^31 bytes or more (seq_len * stride *
+ * 4), ignores the workspace (it may be NULL) and runs as gdn_recurrence_seq.  Source: metrale ssm_gdn_a.rs, launcher
  * `gdn_prefill_regresident` (the operation); the chunked form is exact algebra
  * on logicaffeine gdn.rs `gdn_step`.
  *   workspace        device memory of at least gdn_seq_workspace_bytes(...)
