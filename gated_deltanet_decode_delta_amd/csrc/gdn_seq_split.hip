@@ -190,7 +190,8 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) pr
             const f32x4 Tr = *reinterpret_cast<const f32x4 *>(&t_s[li * kTS + 4 * g]);
             const f32x4 Mr = *reinterpret_cast<const f32x4 *>(&m_s[li * kTS + 4 * g]);
             *reinterpret_cast<f32x4 *>(rec + li * kC + 4 * g) = Tr;
-            *reinterpret_cast<f32x4 *>(rec + 256 + li * kC + 4 * g) = Mr * KQ;   // G[li][4g+r] = M[li][4g+r] k_{4g+r}.q_{li}
+            // G[li][4g+r] = M[li][4g+r] k_{4g+r}.q_{li}, times the output's 1 / sqrt(D)
+            *reinterpret_cast<f32x4 *>(rec + 256 + li * kC + 4 * g) = Mr * KQ * a.scale;
             if (g == 0) rec[512 + li] = be_s[mm][li];
             if (li == 0) *reinterpret_cast<f32x4 *>(rec + 528 + 4 * g) = al_s[mm][0] * Mv;   // P_t = alpha_0 M[t][0]
             if (g == 3) rec[544 + li] = Mv[3];                                             // D[s] = M[15][s]
@@ -375,35 +376,39 @@ __global__ void __launch_bounds__(256) split_kernel(StepArgs a, const float *ws,
         // chunk c + 1 into the buffer chunk c - 1 used (rows past the end are
         // staged too, into a buffer no one reads); visible after the next barrier
         stage(c + 1);
+        const float gc = gam;
         // The strip's chain is split between its halves: half 0 forms
         // R = beta (v - P gam U) and C' = T R and passes C' on through LDS;
         // half 1 forms O = P gam W + G C' and stores the four tokens.  Both
         // update their own columns with C'.
-        f32x4 Cp, O;
+        // X: C' in half 0; in half 1 the first term of O, then C' once read.
+        // One variable for both halves keeps the branch joins free of copies.
+        f32x4 X;
         __builtin_amdgcn_s_setprio(2);   // the strip's dependent chain ahead of other waves' products
         if (half == 0) {
             const f32x4 U = Up + x_s[w ^ 1][0][l];
             f32x4 R;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) R[r] = Br[r] * (vv[r] - Pr[r] * gam * U[r]);
+            for (int r = 0; r < 4; ++r) R[r] = Br[r] * (vv[r] - Pr[r] * gc * U[r]);
             f32x4 c0 = f32x4{0.f, 0.f, 0.f, 0.f}, c1 = c0;
             c0 = mfma(Tr[0], R[0], c0);
             c1 = mfma(Tr[1], R[1], c1);
             c0 = mfma(Tr[2], R[2], c0);
             c1 = mfma(Tr[3], R[3], c1);
-            Cp = c0 + c1;
-            c_s[strip][l] = Cp;
+            X = c0 + c1;
+            c_s[strip][l] = X;
             __builtin_amdgcn_s_setprio(0);
         } else {
             const f32x4 W = Wp + x_s[w ^ 1][1][l];
+            const float gs = gc * a.scale;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) O[r] = Pr[r] * gam * W[r];
+            for (int r = 0; r < 4; ++r) X[r] = Pr[r] * gs * W[r];
         }
         __syncthreads();   // C' visible; chunk c + 1 staged; every read of chunk c - 1's buffers done
         if (half == 1) {
-            Cp = c_s[strip][l];
-            f32x4 o1 = f32x4{0.f, 0.f, 0.f, 0.f};
-            O = mfma(Gr[0], Cp[0], O);
+            const f32x4 Cp = c_s[strip][l];
+            f32x4 O = X, o1 = f32x4{0.f, 0.f, 0.f, 0.f};
+            O = mfma(Gr[0], Cp[0], O);   // G carries the 1 / sqrt(D) of the output
             o1 = mfma(Gr[1], Cp[1], o1);
             O = mfma(Gr[2], Cp[2], O);
             o1 = mfma(Gr[3], Cp[3], o1);
@@ -411,7 +416,8 @@ __global__ void __launch_bounds__(256) split_kernel(StepArgs a, const float *ws,
             const __amdgpu_buffer_rsrc_t ro =
                 buf_rsrc(o0 + (int64_t)t0 * a.out_stride, (int64_t)(T - t0) * a.out_stride * 4);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) buf_store1(ro, o_off + r * o_step, O[r] * a.scale);
+            for (int r = 0; r < 4; ++r) buf_store1(ro, o_off + r * o_step, O[r]);
+            X = Cp;
             __builtin_amdgcn_s_setprio(0);
         }
 
@@ -433,11 +439,11 @@ __global__ void __launch_bounds__(256) split_kernel(StepArgs a, const float *ws,
         }
         gam = gnew;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Cp[r] *= Dr[r] * cscale;
+        for (int r = 0; r < 4; ++r) X[r] *= Dr[r] * cscale;
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
-            for (int m = 0; m < 4; ++m) S[m] = mfma(kcv[4 * s4 + m], Cp[s4], S[m]);
+            for (int m = 0; m < 4; ++m) S[m] = mfma(kcv[4 * s4 + m], X[s4], S[m]);
 
         // loads for the next chunks go out after this chunk's stores
         prefetch_kq(c + 2);
