@@ -305,7 +305,6 @@ __global__ void __launch_bounds__(256) split_kernel(StepArgs a, const float *ws,
     const int lrec = li * kC + 4 * g;
     float vv[4];
     f32x4 Tr, Gr, Br, Pr, Dr;
-    float Plast;
     // Only half 0 uses v (rows past T read 0).  Both halves load the whole
     // record: loading T in one half and G in the other made the compiler keep
     // the pair in scratch.
@@ -324,7 +323,6 @@ __global__ void __launch_bounds__(256) split_kernel(StepArgs a, const float *ws,
         Br = *reinterpret_cast<const f32x4 *>(rec + 512 + 4 * g);
         Pr = *reinterpret_cast<const f32x4 *>(rec + 528 + 4 * g);
         Dr = *reinterpret_cast<const f32x4 *>(rec + 544 + 4 * g);
-        Plast = rec[528 + kC - 1];
     };
 
     // Prologue: chunk 0 staged; chunk 1's k, q and chunk 0's v and record in flight.
@@ -376,7 +374,33 @@ __global__ void __launch_bounds__(256) split_kernel(StepArgs a, const float *ws,
         // chunk c + 1 into the buffer chunk c - 1 used (rows past the end are
         // staged too, into a buffer no one reads); visible after the next barrier
         stage(c + 1);
+        // gam S -> P_15 gam S + K^T (C' diag(D))^T: the decay is kept in gam
+        // while it stays in [2^-60, 2^60] and folded into S otherwise.  Done
+        // here, ahead of the chain (which uses gc, gam at the chunk start), so
+        // that nothing after half 1's stores waits on a load.  P_15 is lane
+        // 48's last P.  1 / gam' comes from the hardware reciprocal: the scale
+        // of one chunk's contribution is off by an ulp or so, far inside the
+        // tolerance, and both halves compute the same value.
         const float gc = gam;
+        // The element goes through an opaque copy first: hipcc (clang 22,
+        // ROCm 7.2) lowers a lane read of element 3 of a four-float vector as
+        // a read of element 0's register.
+        float p15 = Pr[3];
+        asm volatile("" : "+v"(p15));
+        float gnew = gc * __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                        __builtin_bit_cast(int, p15), 48));
+        float cscale;
+        if (__builtin_expect(gnew >= 0x1p-60f && gnew <= 0x1p60f, 1)) {
+            cscale = __builtin_amdgcn_rcpf(gnew);
+        } else {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) S[m] *= gnew;
+            gnew = 1.0f;
+            cscale = 1.0f;
+        }
+        gam = gnew;
+        f32x4 Ds = Dr * cscale;
+        asm volatile("" : "+v"(Ds));   // formed here, before half 1's stores
         // The strip's chain is split between its halves: half 0 forms
         // R = beta (v - P gam U) and C' = T R and passes C' on through LDS;
         // half 1 forms O = P gam W + G C' and stores the four tokens.  Both
@@ -421,25 +445,7 @@ __global__ void __launch_bounds__(256) split_kernel(StepArgs a, const float *ws,
             __builtin_amdgcn_s_setprio(0);
         }
 
-        // gam S -> P_15 gam S + K^T (C' diag(D))^T, the decay kept in gam while
-        // it stays in [2^-60, 2^60] and folded into S otherwise
-        // (1 / gam' by the hardware reciprocal: a relative error of an ulp or so
-        // in the scale of this chunk's contribution, far inside the tolerance;
-        // both halves compute the same value.)
-        float gnew = gam * Plast;
-        float cscale;
-        if (__builtin_expect(gnew >= 0x1p-60f && gnew <= 0x1p60f, 1)) {
-            cscale = __builtin_amdgcn_rcpf(gnew);
-        } else {
-            const float f = gnew;
-#pragma unroll
-            for (int m = 0; m < 4; ++m) S[m] *= f;
-            gnew = 1.0f;
-            cscale = 1.0f;
-        }
-        gam = gnew;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) X[r] *= Dr[r] * cscale;
+        X *= Ds;
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
