@@ -353,21 +353,20 @@ __global__ void __launch_bounds__(256) split_kernel(StepArgs a, const float *ws,
                 for (int m = 0; m < 4; ++m) kcv[4 * s4 + m] = kc[s4 * kKS + 16 * m];
         }
         // partial U^T = K S^T and W^T = Q S^T over this wave's 64 columns
-        f32x4 Ua = f32x4{0.f, 0.f, 0.f, 0.f}, Ub = Ua, Wa = Ua, Wb = Ua;
+        // (one accumulator each: a product accumulating into its own
+        // destination issues back to back)
+        f32x4 Up = f32x4{0.f, 0.f, 0.f, 0.f}, Wp = Up;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int col = 64 * half + 16 * m + 4 * g;
             const f32x4 ka = *reinterpret_cast<const f32x4 *>(&k_s[bb][li * kKS + col]);
             const f32x4 qa = *reinterpret_cast<const f32x4 *>(&q_s[bb][li * kKS + col]);
 #pragma unroll
-            for (int r = 0; r < 4; r += 2) {
-                Ua = mfma(ka[r], S[m][r], Ua);
-                Wa = mfma(qa[r], S[m][r], Wa);
-                Ub = mfma(ka[r + 1], S[m][r + 1], Ub);
-                Wb = mfma(qa[r + 1], S[m][r + 1], Wb);
+            for (int r = 0; r < 4; ++r) {
+                Up = mfma(ka[r], S[m][r], Up);
+                Wp = mfma(qa[r], S[m][r], Wp);
             }
         }
-        const f32x4 Up = Ua + Ub, Wp = Wa + Wb;
         x_s[w][0][l] = Up;
         x_s[w][1][l] = Wp;
         __syncthreads();   // partials visible; every wave is past chunk c - 1
@@ -414,12 +413,9 @@ __global__ void __launch_bounds__(256) split_kernel(StepArgs a, const float *ws,
             f32x4 R;
 #pragma unroll
             for (int r = 0; r < 4; ++r) R[r] = Br[r] * (vv[r] - Pr[r] * gc * U[r]);
-            f32x4 c0 = f32x4{0.f, 0.f, 0.f, 0.f}, c1 = c0;
-            c0 = mfma(Tr[0], R[0], c0);
-            c1 = mfma(Tr[1], R[1], c1);
-            c0 = mfma(Tr[2], R[2], c0);
-            c1 = mfma(Tr[3], R[3], c1);
-            X = c0 + c1;
+            X = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) X = mfma(Tr[r], R[r], X);
             c_s[strip][l] = X;
             __builtin_amdgcn_s_setprio(0);
         } else {
@@ -431,12 +427,9 @@ __global__ void __launch_bounds__(256) split_kernel(StepArgs a, const float *ws,
         __syncthreads();   // C' visible; chunk c + 1 staged; every read of chunk c - 1's buffers done
         if (half == 1) {
             const f32x4 Cp = c_s[strip][l];
-            f32x4 O = X, o1 = f32x4{0.f, 0.f, 0.f, 0.f};
-            O = mfma(Gr[0], Cp[0], O);   // G carries the 1 / sqrt(D) of the output
-            o1 = mfma(Gr[1], Cp[1], o1);
-            O = mfma(Gr[2], Cp[2], O);
-            o1 = mfma(Gr[3], Cp[3], o1);
-            O += o1;
+            f32x4 O = X;   // G carries the 1 / sqrt(D) of the output
+#pragma unroll
+            for (int r = 0; r < 4; ++r) O = mfma(Gr[r], Cp[r], O);
             const __amdgpu_buffer_rsrc_t ro =
                 buf_rsrc(o0 + (int64_t)t0 * a.out_stride, (int64_t)(T - t0) * a.out_stride * 4);
 #pragma unroll
