@@ -169,7 +169,7 @@ def run_seq(g, calls: int):
                              num_k_heads=NK, num_v_heads=NV, head_dim=D)
 
     # after the chip has idled both paths run slower for their first tens of
-    # calls, so each gets 20 warmup calls
+    # calls, so each gets 40 warmup calls and is timed over 100 (sustained use)
     def step_norm(i):   # with z: the gated norm fused into the output
         g.gdn_recurrence_seq_ws(st, t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["z"],
                                 t["gn"], c.eps, out=out, workspace=ws, seq_len=T,
@@ -179,10 +179,10 @@ def run_seq(g, calls: int):
         g.gdn_recurrence_seq(st, t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["z"], t["gn"],
                              c.eps, out=out, seq_len=T, num_k_heads=NK, num_v_heads=NV)
 
-    ms = _timed(step, calls, 20)
-    ms_plain = _timed(step_plain, calls, 20)
-    ms_norm = _timed(step_norm, calls, 5)
-    ms_norm_plain = _timed(step_norm_plain, calls, 5)
+    ms = _timed(step, calls, 40)
+    ms_plain = _timed(step_plain, calls, 40)
+    ms_norm = _timed(step_norm, calls, 40)
+    ms_norm_plain = _timed(step_norm_plain, calls, 40)
     flops = 7.0 * D * D * B * NV * T
     byts = B * T * (2 * NK * D * 4 + NV * (D * 4 + 8 + D * 4)) + 2.0 * B * NV * D * D * 4
     del t, st, out, ws
@@ -647,7 +647,7 @@ def main():
         calibrate_and_profile(g, args.steps)
         return
     if args.seq_only:
-        print(json.dumps(run_seq(g, 20)), flush=True)
+        print(json.dumps(run_seq(g, 100)), flush=True)
         return
 
     m = run_main(g, args.steps, args.warmup, args.pools)
@@ -663,7 +663,7 @@ def main():
                          "median_hbm_frac_algorithmic": round(
                              m["algo_bytes"] / m["trials"][2] / 1e6 / HBM_PEAK_GBS, 4)}}
     wanted = [] if args.no_extra else [w for w in args.extras.split(",") if w]
-    runners = {"fp16_state": lambda: run_fp16(g, 100), "sequence": lambda: run_seq(g, 20),
+    runners = {"fp16_state": lambda: run_fp16(g, 100), "sequence": lambda: run_seq(g, 100),
                "verify": lambda: run_verify(g, 100), "norm_q": lambda: run_norm_q(g, 200),
                "strided": lambda: run_strided(g, 200), "fused": lambda: run_fused(g, 200),
                "real_head": lambda: run_real_head(g, 50)}
