@@ -185,7 +185,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) pr
                 for (int t = 0; t < kC; ++t) t_s[t * kTS + li] = x[t];
             }
             __syncthreads();
-            // workspace record: T row-major, G row-major, beta, P, D
+            // workspace record: T row-major, G / sqrt(D) row-major, beta, P, D
             float *rec = ws + (((int64_t)b * a.nv + h) * nc + c) * kSeqRec;
             const f32x4 Tr = *reinterpret_cast<const f32x4 *>(&t_s[li * kTS + 4 * g]);
             const f32x4 Mr = *reinterpret_cast<const f32x4 *>(&m_s[li * kTS + 4 * g]);
