@@ -209,3 +209,26 @@ def test_large_pool_fused_two_buffers(g):
         assert np.array_equal(host(ring_out[b:b + 1])[:, :live], ring[:, :live]), b
         assert out_err(got_y[b:b + 1], ref, NV, D) < TOL_STEP, b
         assert tile_err(host(st[b:b + 1]), ref_st, NV, D) < TOL_STEP, b
+
+
+def test_sequence_rows_past_2_31_bytes(g, seq):
+    """The rows of one sequence span more than 2**31 bytes of v: 40 tokens
+    with a v row stride of 2**24 + 256 elements.  The workspace entry point
+    then runs without its workspace (its state pass addresses a sequence's
+    rows with 32-bit byte offsets); both entry points match the oracle."""
+    import torch
+    T, nk, nv = 40, 1, 2
+    vs = 2 ** 24 + 256
+    assert T * vs * 4 > 2 ** 31 - 1
+    c = inputs.make_case(2107, B=1, NK=nk, NV=nv, D=D, T=T)
+    say("sequence, v rows past 2**31 bytes", T, vs)
+    big = torch.zeros((T, vs), dtype=torch.float32, device=DEV)   # 2.7 GB
+    big[:, :nv * D] = dev(np.ascontiguousarray(c.v.reshape(T, nv * D)))
+    v = big[:, :nv * D]
+    st = dev(c.state)
+    q, k, al, be = (dev(getattr(c, n)) for n in ("q", "k", "alpha", "beta"))
+    o = seq(st, q, k, v, al, be, seq_len=T, num_k_heads=nk, num_v_heads=nv, head_dim=D)
+    ref_st = c.state.copy()
+    ref = orc.seq(ref_st, c.q, c.k, c.v, c.alpha, c.beta, B=1, T=T, NK=nk, NV=nv, Dk=D, Dv=D)
+    assert out_err(host(o), ref, nv, D) < TOL_STEP * T
+    assert tile_err(host(st), ref_st, nv, D) < TOL_STEP * T
