@@ -298,7 +298,7 @@ __global__ void __launch_bounds__(256) split_kernel(StepArgs a, const float *ws,
         }
     };
     // per-chunk data of the lane: v of its row for tokens 4g .. 4g+3, and the
-    // workspace record (T[li][4g..], G[li][4g..], beta, P, D at 4g.., P_15)
+    // workspace record (T[li][4g..], G[li][4g..], beta, P, D at 4g..)
     const int64_t v0 = row_base * a.v_stride + (int64_t)h * kD;
     const int v_off = (int)((4 * g * a.v_stride + row) * 4);
     const int v_step = (int)(a.v_stride * 4);
