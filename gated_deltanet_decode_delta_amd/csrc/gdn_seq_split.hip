@@ -226,8 +226,8 @@ __device__ inline void buf_store1(__amdgpu_buffer_rsrc_t r, int off, float x) {
 // indices equal modulo 8, so they run on one XCD and share its L2 for the
 // head's workspace records and k, q rows.
 __global__ void __launch_bounds__(256) split_kernel(StepArgs a, const float *ws, int nc) {
-    __shared__ __align__(16) float k_s[2][kC * kKS], q_s[2][kC * kKS];
-    __shared__ f32x4 x_s[4][2][64];   // partial U, W of each wave
+    __shared__ __align__(16) float kq_s[2][2][kC * kKS];   // [buffer][k, q] of a chunk
+    __shared__ f32x4 x_s[4][64];      // each wave's partial that its partner needs
     __shared__ f32x4 c_s[2][64];      // C' of each strip
 
     const int tid = threadIdx.x;
@@ -293,8 +293,8 @@ __global__ void __launch_bounds__(256) split_kernel(StepArgs a, const float *ws,
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int f = tid + 256 * u;
-            *reinterpret_cast<f32x4 *>(&k_s[bb][(f >> 5) * kKS + (f & 31) * 4]) = pk[u];
-            *reinterpret_cast<f32x4 *>(&q_s[bb][(f >> 5) * kKS + (f & 31) * 4]) = pq[u];
+            *reinterpret_cast<f32x4 *>(&kq_s[bb][0][(f >> 5) * kKS + (f & 31) * 4]) = pk[u];
+            *reinterpret_cast<f32x4 *>(&kq_s[bb][1][(f >> 5) * kKS + (f & 31) * 4]) = pq[u];
         }
     };
     // per-chunk data of the lane: v of its row for tokens 4g .. 4g+3, and the
@@ -346,29 +346,30 @@ __global__ void __launch_bounds__(256) split_kernel(StepArgs a, const float *ws,
         // requested now so that their LDS latency is long past at the update
         float kcv[16];
         {
-            const float *kc = &k_s[bb][4 * g * kKS + 64 * half + li];
+            const float *kc = &kq_s[bb][0][4 * g * kKS + 64 * half + li];
 #pragma unroll
             for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
                 for (int m = 0; m < 4; ++m) kcv[4 * s4 + m] = kc[s4 * kKS + 16 * m];
         }
-        // partial U^T = K S^T and W^T = Q S^T over this wave's 64 columns
-        // (one accumulator each: a product accumulating into its own
-        // destination issues back to back)
-        f32x4 Up = f32x4{0.f, 0.f, 0.f, 0.f}, Wp = Up;
+        // partial U^T = K S^T and W^T = Q S^T over this wave's 64 columns,
+        // one accumulator each (a product accumulating into its own
+        // destination issues back to back).  Mp is the one the wave goes on
+        // with (U in half 0, W in half 1), Xp the one its partner needs: the
+        // operand rows are picked by half, so no select of results is needed.
+        f32x4 Mp = f32x4{0.f, 0.f, 0.f, 0.f}, Xp = Mp;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int col = 64 * half + 16 * m + 4 * g;
-            const f32x4 ka = *reinterpret_cast<const f32x4 *>(&k_s[bb][li * kKS + col]);
-            const f32x4 qa = *reinterpret_cast<const f32x4 *>(&q_s[bb][li * kKS + col]);
+            const f32x4 ma = *reinterpret_cast<const f32x4 *>(&kq_s[bb][half][li * kKS + col]);
+            const f32x4 xa = *reinterpret_cast<const f32x4 *>(&kq_s[bb][half ^ 1][li * kKS + col]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                Up = mfma(ka[r], S[m][r], Up);
-                Wp = mfma(qa[r], S[m][r], Wp);
+                Mp = mfma(ma[r], S[m][r], Mp);
+                Xp = mfma(xa[r], S[m][r], Xp);
             }
         }
-        x_s[w][0][l] = Up;
-        x_s[w][1][l] = Wp;
+        x_s[w][l] = Xp;
         __syncthreads();   // partials visible; every wave is past chunk c - 1
         // chunk c + 1 into the buffer chunk c - 1 used (rows past the end are
         // staged too, into a buffer no one reads); visible after the next barrier
@@ -409,7 +410,7 @@ __global__ void __launch_bounds__(256) split_kernel(StepArgs a, const float *ws,
         f32x4 X;
         __builtin_amdgcn_s_setprio(2);   // the strip's dependent chain ahead of other waves' products
         if (half == 0) {
-            const f32x4 U = Up + x_s[w ^ 1][0][l];
+            const f32x4 U = Mp + x_s[w ^ 1][l];
             f32x4 R;
 #pragma unroll
             for (int r = 0; r < 4; ++r) R[r] = Br[r] * (vv[r] - Pr[r] * gc * U[r]);
@@ -419,7 +420,7 @@ __global__ void __launch_bounds__(256) split_kernel(StepArgs a, const float *ws,
             c_s[strip][l] = X;
             __builtin_amdgcn_s_setprio(0);
         } else {
-            const f32x4 W = Wp + x_s[w ^ 1][1][l];
+            const f32x4 W = Mp + x_s[w ^ 1][l];
             const float gs = gc * a.scale;
 #pragma unroll
             for (int r = 0; r < 4; ++r) X[r] = Pr[r] * gs * W[r];
