@@ -52,14 +52,6 @@ def _load():
         build()
     lib = ctypes.CDLL(_LIB)
     i64, i32, dbl, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_void_p
-    lib.orc_f64_to_f16.restype = ctypes.c_uint16
-    lib.orc_f64_to_f16.argtypes = [dbl]
-    lib.orc_f16_to_f64.restype = dbl
-    lib.orc_f16_to_f64.argtypes = [ctypes.c_uint16]
-    lib.orc_f64_to_bf16.restype = ctypes.c_uint16
-    lib.orc_f64_to_bf16.argtypes = [dbl]
-    lib.orc_bf16_to_f64.restype = dbl
-    lib.orc_bf16_to_f64.argtypes = [ctypes.c_uint16]
     for name in ("orc_f32_to_f16_array", "orc_f16_to_f32_array", "orc_f64_to_bf16_array"):
         getattr(lib, name).restype = None
         getattr(lib, name).argtypes = [vp, vp, i64]
@@ -125,22 +117,6 @@ def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     dst = np.empty(src.shape, dtype=np.uint16)
     _load().orc_f64_to_bf16_array(_ptr(src), _ptr(dst), src.size)
     return dst
-
-
-def f64_to_f16(x: float) -> int:
-    return int(_load().orc_f64_to_f16(float(x)))
-
-
-def f16_to_f64(h: int) -> float:
-    return float(_load().orc_f16_to_f64(int(h)))
-
-
-def f64_to_bf16(x: float) -> int:
-    return int(_load().orc_f64_to_bf16(float(x)))
-
-
-def bf16_to_f64(h: int) -> float:
-    return float(_load().orc_bf16_to_f64(int(h)))
 
 
 # --------------------------------------------------------------------------

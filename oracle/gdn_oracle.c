@@ -113,16 +113,6 @@ uint16_t orc_f64_to_bf16(double x)
     return (uint16_t)(sign | (uint16_t)((e + 127) << 7) | (uint16_t)(m - 128.0));
 }
 
-double orc_bf16_to_f64(uint16_t h)
-{
-    double s = (h & 0x8000u) ? -1.0 : 1.0;
-    int e = (h >> 7) & 0xff;
-    int f = h & 0x7f;
-    if (e == 0xff) return f ? NAN : s * INFINITY;
-    if (e == 0) return s * ldexp((double)f, -133);
-    return s * ldexp((double)(128 + f), e - 134);
-}
-
 void orc_f32_to_f16_array(const float *src, uint16_t *dst, int64_t n)
 {
     for (int64_t i = 0; i < n; ++i) dst[i] = orc_f64_to_f16((double)src[i]);

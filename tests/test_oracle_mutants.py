@@ -29,6 +29,8 @@ MUTANTS = {
     "sigmoid_sign": ("z[i] / (1.0 + exp(-z[i]))", "z[i] / (1.0 + exp(z[i]))"),
     "norm_weight_dropped": ("(gn[i] * o[i] / r)", "(o[i] / r)"),
     "f16_truncates": ("double m = nearbyint(ldexp(a, 10 - e));", "double m = floor(ldexp(a, 10 - e));"),
+    "bf16_truncates": ("double m = nearbyint(ldexp(a, 7 - e));", "double m = floor(ldexp(a, 7 - e));"),
+    "bf16_subnormal_flush": ("double m = nearbyint(ldexp(a, 133));", "double m = 0.0;"),
     "f16_subnormal_flush": ("double m = nearbyint(ldexp(a, 24));", "double m = 0.0;"),
     "no_per_step_rounding": ("if (state_kind == ORC_STATE_F32) S[e] = (double)(float)S[e];",
                              "if (state_kind == ORC_STATE_F32) S[e] = S[e];"),
