@@ -134,15 +134,36 @@ def run_fp16(g, calls: int):
         g.gdn_decode_f16state(st16, t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["z"], t["gn"],
                               c.eps, out=out, num_k_heads=NK, num_v_heads=NV)
 
-    ms = _timed(step, calls, 5)
+    # 5 trials of `calls` calls each after a warmup; the median trial is the figure
+    trials = sorted(_timed(step, calls, 5) for _ in range(5))
+    ms = trials[2]
     state_bytes = 2.0 * B * NV * D * D * 2
     algo = B * NV * head_bytes(D, NV, NK, 2, 2, True)
     del st16, t, out
     torch.cuda.empty_cache()
     return {"workload": "fp16 state decode, B=256, NV=48, NK=16, D=128, fused norm, bf16 out",
-            "ms_per_call": round(ms, 5), "state_GBps": round(state_bytes / ms / 1e6, 1),
+            "ms_per_call": round(ms, 5), "trials": f"median of 5 trials x {calls} calls",
+            "min_ms_per_call": round(trials[0], 5),
+            "state_GBps": round(state_bytes / ms / 1e6, 1),
             "hbm_frac_algorithmic": round(algo / ms / 1e6 / HBM_PEAK_GBS, 4),
             "tokens_per_s_batch": round(B / ms * 1e3, 1)}
+
+
+def _cold_calls(fn, trials: int, pause_s: float):
+    """Single synchronised calls, each after the GPU has idled ``pause_s``
+    seconds: ms of each call, sorted."""
+    import torch
+    out = []
+    for i in range(trials):
+        torch.cuda.synchronize()
+        time.sleep(pause_s)
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        fn(i)
+        end.record()
+        torch.cuda.synchronize()
+        out.append(start.elapsed_time(end))
+    return sorted(out)
 
 
 def run_seq(g, calls: int):
@@ -169,8 +190,9 @@ def run_seq(g, calls: int):
                              num_k_heads=NK, num_v_heads=NV, head_dim=D)
 
     # after the chip has idled both paths run slower for their first tens of
-    # calls, so each gets 40 warmup calls and is timed over 100 (sustained use)
-    def step_norm(i):   # with z: the gated norm fused into the output
+    # calls, so each gets 40 warmup calls and is timed over 100 (sustained
+    # use); single calls after an idle pause are reported beside that
+    def step_norm(i):   # with z: the raw pass, then the gated-norm pass over the output rows
         g.gdn_recurrence_seq_ws(st, t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["z"],
                                 t["gn"], c.eps, out=out, workspace=ws, seq_len=T,
                                 num_k_heads=NK, num_v_heads=NV)
@@ -179,6 +201,8 @@ def run_seq(g, calls: int):
         g.gdn_recurrence_seq(st, t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["z"], t["gn"],
                              c.eps, out=out, seq_len=T, num_k_heads=NK, num_v_heads=NV)
 
+    cold = _cold_calls(step, 5, 1.0)
+    cold_plain = _cold_calls(step_plain, 5, 1.0)
     ms = _timed(step, calls, 40)
     ms_plain = _timed(step_plain, calls, 40)
     ms_norm = _timed(step_norm, calls, 40)
@@ -192,9 +216,16 @@ def run_seq(g, calls: int):
             "ms_per_call": round(ms, 4), "tflops": round(flops / ms / 1e9, 2),
             "fp32_matrix_frac": round(flops / ms / 1e9 / FP32_VALU_PEAK_TFLOPS, 4),
             "GBps": round(byts / ms / 1e6, 1), "tokens_per_s": round(B * T / ms * 1e3, 1),
+            "timing": f"sustained: {calls} calls after 40 warmup; cold: 1 call x 5 trials, "
+                      "each after 1 s idle",
+            "cold_single_call_ms": {"median": round(cold[2], 4), "min": round(cold[0], 4)},
             "no_workspace_ms_per_call": round(ms_plain, 4),
-            "z_fused_norm_ms_per_call": round(ms_norm, 4),
-            "z_fused_norm_no_workspace_ms_per_call": round(ms_norm_plain, 4)}
+            "no_workspace_tflops": round(flops / ms_plain / 1e9, 2),
+            "no_workspace_fp32_matrix_frac": round(flops / ms_plain / 1e9 / FP32_VALU_PEAK_TFLOPS, 4),
+            "no_workspace_cold_single_call_ms": {"median": round(cold_plain[2], 4),
+                                                 "min": round(cold_plain[0], 4)},
+            "z_raw_then_norm_pass_ms_per_call": round(ms_norm, 4),
+            "z_raw_then_norm_pass_no_workspace_ms_per_call": round(ms_norm_plain, 4)}
 
 
 def run_verify(g, calls: int, pools: int = 16):

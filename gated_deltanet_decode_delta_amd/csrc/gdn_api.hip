@@ -143,25 +143,36 @@ gdn_status check_extra_out(const Spans &sp, const void *p, int64_t rows, int64_t
     return GDN_OK;
 }
 
+// A call with a single row never steps to a second one, so validate() leaves
+// its strides unchecked; the kernels still size buffer ranges from them.  Here
+// each such stride is raised to at least its row width (row 0 is unchanged),
+// so every kernel sees strides that hold their rows.
+int64_t row_stride(const Call &c, int64_t stride, int64_t width) {
+    const bool single = (int64_t)c.batch * c.seq_len <= 1;
+    return single && stride < width ? width : stride;
+}
+
 gdn::StepArgs to_args(const Call &c, void *state, void *out) {
+    const int64_t vw = (int64_t)c.nv * c.dv;
     gdn::StepArgs a;
     a.state = state;
-    a.pitch = c.pitch;
+    a.pitch = c.batch <= 1 && c.pitch < (int64_t)c.nv * c.dk * c.dv ? (int64_t)c.nv * c.dk * c.dv
+                                                                    : c.pitch;
     a.q = c.q;
     a.k = c.k;
-    a.qk_stride = c.qk_stride;
+    a.qk_stride = row_stride(c, c.qk_stride, (int64_t)c.nk * c.dk);
     a.v = c.v;
-    a.v_stride = c.v_stride;
+    a.v_stride = row_stride(c, c.v_stride, vw);
     a.alpha = c.alpha;
     a.beta = c.beta;
-    a.ab_stride = c.ab_stride;
+    a.ab_stride = row_stride(c, c.ab_stride, c.nv);
     a.z = c.z;
-    a.z_stride = c.z_stride;
+    a.z_stride = row_stride(c, c.z_stride, vw);
     a.gn = c.gn;
     a.eps = c.eps;
     a.scale = (float)(1.0 / sqrt((double)c.dk));
     a.out = out;
-    a.out_stride = c.out_stride;
+    a.out_stride = row_stride(c, c.out_stride, vw);
     a.codes = nullptr;
     a.codes_stride = 0;
     a.scales = nullptr;
@@ -319,15 +330,17 @@ gdn_status gdn_recurrence_seq_ws(float *state, int64_t state_seq_stride, const f
     // The split path launches one pre-pass workgroup per (sequence, key head,
     // chunk), four state-pass workgroups per value head and one norm workgroup
     // per 16 (row, head) pairs, and the state pass reads q, k, v and writes o
-    // through buffer descriptors with 32-bit offsets.  A shape whose grids
-    // would not fit 32 bits, whose rows of one sequence span 2^31 bytes or
-    // more in q, k, v or o, or another head dim, runs the kernels without a
-    // workspace.
+    // through buffer descriptors with 32-bit offsets.  Those offsets reach the
+    // last row of a whole 16-token chunk, padding rows past the end included,
+    // so they must fit 32 bits over max(T, 16) rows.  A shape whose grids would
+    // not fit 32 bits, whose rows of one sequence (at least 16 of them) span
+    // 2^31 bytes or more in q, k, v or o, or another head dim, runs the
+    // kernels without a workspace.
     const int64_t widest = std::max(a.qk_stride, std::max(a.v_stride, a.out_stride));
     if (k_dim != 128 || (int64_t)batch * num_k_heads * ((seq_len + 15) / 16) > INT32_MAX ||
         (int64_t)batch * num_v_heads * 4 > INT32_MAX ||
         ((int64_t)batch * seq_len * num_v_heads + 15) / 16 > INT32_MAX ||
-        (int64_t)seq_len * widest * 4 > INT32_MAX)
+        (int64_t)std::max(seq_len, 16) * widest * 4 + 1024 > INT32_MAX)
         return finish(gdn::launch_seq(a, k_dim, norm ? gdn::kOutNormF32 : gdn::kOutRawF32,
                                       (hipStream_t)stream));
     const int64_t need = gdn_seq_workspace_bytes(batch, seq_len, num_v_heads, k_dim, v_dim);

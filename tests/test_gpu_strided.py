@@ -114,3 +114,69 @@ def test_verify_packed_rows(g, D):
         orc.seq(st_t, pre(c.q), pre(c.k), pre(c.v), pre(c.alpha), pre(c.beta), B=B, T=n, NK=NK,
                 NV=NV, Dk=D, Dv=D)
         assert tile_err(got[:, t], st_t, NV, D) < TOL_CHAIN, t
+
+
+def _seq_ws_raw(g, st, q, k, qk_stride, v, v_stride, al, be, ab_stride, out, out_stride, B, T,
+                NK, NV, D):
+    """gdn_recurrence_seq_ws straight through ctypes, strides exactly as given."""
+    import torch
+    lib = g.lib()
+    need = lib.gdn_seq_workspace_bytes(B, T, NV, D, D)
+    ws = torch.empty(max(need, 16) // 4, dtype=torch.float32, device="cuda:0")
+    s = lib.gdn_recurrence_seq_ws(st.data_ptr(), NV * D * D, q.data_ptr(), k.data_ptr(), qk_stride,
+                                  v.data_ptr(), v_stride, al.data_ptr(), be.data_ptr(), ab_stride,
+                                  None, 0, None, 0.0, out.data_ptr(), out_stride, B, T, NK, NV, D,
+                                  D, ws.data_ptr(), need,
+                                  torch.cuda.current_stream().cuda_stream)
+    assert s == 0, g.STATUS_NAMES.get(s, s)
+
+
+@pytest.mark.parametrize("qk_stride", [0, 2 * 16 * 128])
+def test_seq_ws_single_row_small_strides(g, qk_stride):
+    """One sequence of one token takes no stride check (there is no second
+    row), so strides of 0 are legal; the workspace path must still read every
+    input of that row and write its output (regression: its buffer ranges were
+    once sized from the stride, so everything read as 0)."""
+    import torch
+    B, T, NK, NV, D = 1, 1, 16, 48, 128
+    c = inputs.make_case(1900 + qk_stride, B=B, NK=NK, NV=NV, D=D, T=T)
+    say("seq_ws single row, qk stride", qk_stride)
+    st = dev(c.state)
+    if qk_stride:   # q | k of one row side by side: k read at q + NK * D
+        qk = dev(np.concatenate([c.q, c.k], axis=1))
+        q, k = qk[:, :NK * D], qk[:, NK * D:]
+    else:
+        q, k = dev(c.q), dev(c.k)
+    out = torch.full((1, NV * D), float("nan"), device="cuda:0")
+    _seq_ws_raw(g, st, q, k, qk_stride, dev(c.v), 0, dev(c.alpha), dev(c.beta), 0, out, 0,
+                B, T, NK, NV, D)
+    ref_st = c.state.copy()
+    ref = orc.seq(ref_st, c.q, c.k, c.v, c.alpha, c.beta, B=B, T=T, NK=NK, NV=NV, Dk=D, Dv=D)
+    assert out_err(host(out), ref, NV, D) < 1e-5
+    assert tile_err(host(st), ref_st, NV, D) < 1e-5
+
+
+@pytest.mark.parametrize("T,out_stride", [(1, (1 << 28) + 64), (2, 40_000_000), (5, 36_000_000)])
+def test_seq_ws_wide_output_stride_short_sequence(g, T, out_stride):
+    """Output rows so far apart that the offsets of a whole 16-token chunk pass
+    2^31 bytes although T rows do not: the call must still be exact, and
+    nothing between the rows may be written (regression: the 32-bit lane
+    offsets of the padding tokens once wrapped into the valid range)."""
+    import torch
+    B, NK, NV, D = 1, 16, 48, 128
+    vw = NV * D
+    c = inputs.make_case(1950 + T, B=B, NK=NK, NV=NV, D=D, T=T)
+    say("seq_ws wide output stride", T, out_stride)
+    st = dev(c.state)
+    buf = torch.full(((T - 1) * out_stride + vw,), float("nan"), device="cuda:0")
+    _seq_ws_raw(g, st, dev(c.q), dev(c.k), NK * D, dev(c.v), vw, dev(c.alpha), dev(c.beta), NV,
+                buf, out_stride, B, T, NK, NV, D)
+    torch.cuda.synchronize()
+    rows = torch.stack([buf[t * out_stride:t * out_stride + vw] for t in range(T)])
+    ref_st = c.state.copy()
+    ref = orc.seq(ref_st, c.q, c.k, c.v, c.alpha, c.beta, B=B, T=T, NK=NK, NV=NV, Dk=D, Dv=D)
+    assert out_err(host(rows), ref, NV, D) < TOL_CHAIN
+    assert tile_err(host(st), ref_st, NV, D) < TOL_CHAIN
+    for t in range(T - 1):
+        gap = buf[t * out_stride + vw:(t + 1) * out_stride]
+        assert bool(torch.isnan(gap).all()), t
