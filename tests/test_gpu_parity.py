@@ -17,7 +17,7 @@ import pytest
 
 import oracle as orc
 from gated_deltanet_decode_delta_amd import inputs
-from gpu_util import bf16_ok, dev, host, out_err, tile_err
+from gpu_util import bf16_ok, dev, host, normed_output_errors, out_err, tile_err
 
 pytestmark = pytest.mark.gpu
 
@@ -171,7 +171,18 @@ def test_batched_padded_pool_100_calls(g):
     got_state, got_y = host(st), host(y)
     assert np.isnan(got_state[:, NV * D * D:]).all()
     assert tile_err(got_state, ref_state, NV, D) < TOL_CHAIN
-    assert out_err(got_y, ref_last, NV, D) < TOL_CHAIN
+    # The same inputs 100 times drive each head's state toward v k^T, so o = S'q
+    # becomes a cancellation where k.q is near 0 (condition numbers up to ~2e4
+    # here): fp32 evaluation of any order then errs by ~1e-3 relative to |o|.
+    # Every head is held to the tolerance relative to the size of o's summands;
+    # heads whose output is not such a cancellation (kappa <= 100) also to the
+    # plain measure relative to |y|.
+    plain, scaled, kappa = normed_output_errors(got_y, ref_last, ref_state, c.q, c.z, c.gn, NV,
+                                                NK, D, c.eps)
+    assert scaled.max() < TOL_CHAIN, (scaled.max(), int(scaled.argmax()))
+    well = kappa <= 100
+    assert well.sum() > 0.9 * well.size
+    assert plain[well].max() < TOL_CHAIN, (plain[well].max(), kappa[well].max())
     del torch
 
 
