@@ -32,10 +32,11 @@ GDN_BF16 = 1
 STATUS_NAMES = {
     0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_STRIDE",
     4: "GDN_ERR_UNSUPPORTED", 5: "GDN_ERR_ALIAS", 6: "GDN_ERR_DTYPE", 7: "GDN_ERR_HIP",
-    8: "GDN_ERR_ARG",
+    8: "GDN_ERR_ARG", 9: "GDN_ERR_SCRATCH",
 }
 EXPORTS = ("gdn_decode", "gdn_decode_norm", "gdn_decode_norm_q", "gdn_decode_f16state",
-           "gdn_recurrence_seq", "gdn_recurrence_seq_ws", "gdn_seq_workspace_bytes",
+           "gdn_recurrence_seq", "gdn_recurrence_seq_ws", "gdn_recurrence_seq_noalloc",
+           "gdn_seq_workspace_bytes",
            "gdn_decode_verify", "gdn_decode_fused", "gdn_state_f32_to_f16",
            "gdn_state_f16_to_f32", "gdn_status_string", "gdn_last_hip_error")
 VERIFY_MAX_TOKENS = 8
@@ -73,6 +74,7 @@ def _lib():
                                        f32, vp, i64, i32, i32, i32, i32, i32, i32, vp]
     lib.gdn_recurrence_seq_ws.argtypes = [vp, i64, vp, vp, i64, vp, i64, vp, vp, i64, vp, i64, vp,
                                           f32, vp, i64, i32, i32, i32, i32, i32, i32, vp, i64, vp]
+    lib.gdn_recurrence_seq_noalloc.argtypes = lib.gdn_recurrence_seq.argtypes
     lib.gdn_seq_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.gdn_decode_norm_q.argtypes = [vp, i64, vp, vp, i64, vp, i64, vp, vp, i64, vp, i64, vp, f32,
                                       vp, i64, vp, i64, vp, i64, i32, i32, i32, i32, i32, vp]
@@ -360,6 +362,23 @@ def gdn_recurrence_seq_ws(state, q, k, v, alpha, beta, z=None, norm_weight=None,
     nbytes = workspace.numel() * workspace.element_size()
     _check(_lib().gdn_recurrence_seq_ws(*head, float(eps), *tail, workspace.data_ptr(), nbytes,
                                         _stream(state, stream)), "gdn_recurrence_seq_ws")
+    return out
+
+
+# bytes of the library's static scratch behind gdn_recurrence_seq_noalloc, per GPU
+SEQ_NOALLOC_MAX_BYTES = 64 << 20
+
+
+def gdn_recurrence_seq_noalloc(state, q, k, v, alpha, beta, z=None, norm_weight=None,
+                               eps: float = 1e-6, out=None, *, seq_len: int, num_k_heads: int,
+                               num_v_heads: int, head_dim: Optional[int] = None, stream=None):
+    """``gdn_recurrence_seq_ws`` with the workspace in the library's static
+    scratch (at most ``SEQ_NOALLOC_MAX_BYTES``); calls on one GPU must not
+    overlap.  ``out`` is allocated here when not given."""
+    out, head, tail = _seq_args(state, q, k, v, alpha, beta, z, norm_weight, out, seq_len,
+                                num_k_heads, num_v_heads, head_dim)
+    _check(_lib().gdn_recurrence_seq_noalloc(*head, float(eps), *tail, _stream(state, stream)),
+           "gdn_recurrence_seq_noalloc")
     return out
 
 

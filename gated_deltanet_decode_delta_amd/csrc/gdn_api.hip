@@ -7,6 +7,7 @@
 // synchronisation, no printing.
 #include <algorithm>
 #include <math.h>
+#include <mutex>
 #include <stdint.h>
 
 #include "../../include/gdn.h"
@@ -309,6 +310,66 @@ int64_t gdn_seq_workspace_bytes(int32_t batch, int32_t seq_len, int32_t num_v_he
     return (int64_t)bytes;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Whether a validated sequence call takes the workspace path (D = 128, split
+// state pass).  That path launches one pre-pass workgroup per (sequence, key
+// head, chunk), four state-pass workgroups per value head and one norm
+// workgroup per 16 (row, head) pairs, and the state pass reads q, k, v and
+// writes o through buffer descriptors with 32-bit offsets.  Those offsets reach
+// the last row of a whole 16-token chunk, padding rows past the end included,
+// so they must fit 32 bits over max(T, 16) rows.  A shape whose grids would not
+// fit 32 bits, whose rows of one sequence (at least 16 of them) span 2^31 bytes
+// or more in q, k, v or o, or another head dim, runs the kernels without a
+// workspace.
+bool seq_split_path(const gdn::StepArgs &a, int32_t k_dim) {
+    const int64_t widest = std::max(a.qk_stride, std::max(a.v_stride, a.out_stride));
+    return !(k_dim != 128 || (int64_t)a.batch * a.nk * ((a.seq_len + 15) / 16) > INT32_MAX ||
+             (int64_t)a.batch * a.nv * 4 > INT32_MAX ||
+             ((int64_t)a.batch * a.seq_len * a.nv + 15) / 16 > INT32_MAX ||
+             (int64_t)std::max(a.seq_len, 16) * widest * 4 + 1024 > INT32_MAX);
+}
+
+}  // namespace
+
+// Scratch memory of gdn_recurrence_seq_noalloc: the workspace records of the
+// split sequence path in the library's own device memory, so that the call
+// allocates nothing.  Each GPU the library runs on holds its own copy, loaded
+// with the code object and kept until the process ends.  Host code never uses
+// this name as an address: the device address comes from hipGetSymbolAddress,
+// once per device (scratch_address below).
+static __device__ __align__(256) float scratch[GDN_SEQ_NOALLOC_MAX_BYTES / 4];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device, resolved on the
+// first call there (with that device current) and kept per device.
+hipError_t scratch_address(float **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = static_cast<float *>(g_scratch_ptr[dev]);
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
 gdn_status gdn_recurrence_seq_ws(float *state, int64_t state_seq_stride, const float *q,
                                  const float *k, int64_t qk_stride, const float *v,
                                  int64_t v_stride, const float *alpha, const float *beta,
@@ -327,20 +388,7 @@ gdn_status gdn_recurrence_seq_ws(float *state, int64_t state_seq_stride, const f
     gdn_status s = validate(c, &empty, &sp);
     if (s != GDN_OK || empty) return s;
     gdn::StepArgs a = to_args(c, state, out);
-    // The split path launches one pre-pass workgroup per (sequence, key head,
-    // chunk), four state-pass workgroups per value head and one norm workgroup
-    // per 16 (row, head) pairs, and the state pass reads q, k, v and writes o
-    // through buffer descriptors with 32-bit offsets.  Those offsets reach the
-    // last row of a whole 16-token chunk, padding rows past the end included,
-    // so they must fit 32 bits over max(T, 16) rows.  A shape whose grids would
-    // not fit 32 bits, whose rows of one sequence (at least 16 of them) span
-    // 2^31 bytes or more in q, k, v or o, or another head dim, runs the
-    // kernels without a workspace.
-    const int64_t widest = std::max(a.qk_stride, std::max(a.v_stride, a.out_stride));
-    if (k_dim != 128 || (int64_t)batch * num_k_heads * ((seq_len + 15) / 16) > INT32_MAX ||
-        (int64_t)batch * num_v_heads * 4 > INT32_MAX ||
-        ((int64_t)batch * seq_len * num_v_heads + 15) / 16 > INT32_MAX ||
-        (int64_t)std::max(seq_len, 16) * widest * 4 + 1024 > INT32_MAX)
+    if (!seq_split_path(a, k_dim))
         return finish(gdn::launch_seq(a, k_dim, norm ? gdn::kOutNormF32 : gdn::kOutRawF32,
                                       (hipStream_t)stream));
     const int64_t need = gdn_seq_workspace_bytes(batch, seq_len, num_v_heads, k_dim, v_dim);
@@ -351,6 +399,36 @@ gdn_status gdn_recurrence_seq_ws(float *state, int64_t state_seq_stride, const f
     s = check_extra_out(sp, workspace, 1, need / 4, need / 4, 4, 16, &ws);
     if (s != GDN_OK) return s;
     return finish(gdn::launch_seq_split(a, static_cast<float *>(workspace), (hipStream_t)stream));
+}
+
+gdn_status gdn_recurrence_seq_noalloc(float *state, int64_t state_seq_stride, const float *q,
+                                      const float *k, int64_t qk_stride, const float *v,
+                                      int64_t v_stride, const float *alpha, const float *beta,
+                                      int64_t ab_stride, const float *z, int64_t z_stride,
+                                      const float *norm_weight, float eps, float *out,
+                                      int64_t out_stride, int32_t batch, int32_t seq_len,
+                                      int32_t num_k_heads, int32_t num_v_heads, int32_t k_dim,
+                                      int32_t v_dim, void *stream) {
+    const bool norm = z != nullptr;
+    Call c{state, state_seq_stride, 4, q, k, qk_stride, v, v_stride, alpha, beta, ab_stride,
+           z, z_stride, norm_weight, eps, norm, out, 4, out_stride,
+           batch, seq_len, num_k_heads, num_v_heads, k_dim, v_dim};
+    bool empty;
+    gdn_status s = validate(c, &empty);
+    if (s != GDN_OK || empty) return s;
+    gdn::StepArgs a = to_args(c, state, out);
+    if (!seq_split_path(a, k_dim))
+        return finish(gdn::launch_seq(a, k_dim, norm ? gdn::kOutNormF32 : gdn::kOutRawF32,
+                                      (hipStream_t)stream));
+    const int64_t need = gdn_seq_workspace_bytes(batch, seq_len, num_v_heads, k_dim, v_dim);
+    if (need < 0) return GDN_ERR_SHAPE;
+    if (need > (int64_t)GDN_SEQ_NOALLOC_MAX_BYTES) return GDN_ERR_SCRATCH;
+    // every record the state pass reads is written by the pre-pass of the same
+    // call first, so nothing in the scratch has to start at zero
+    float *ws = nullptr;
+    const hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess) return finish(e);
+    return finish(gdn::launch_seq_split(a, ws, (hipStream_t)stream));
 }
 
 gdn_status gdn_decode_verify(float *state, int64_t state_seq_stride, float *inter_state,
@@ -515,6 +593,9 @@ const char *gdn_status_string(gdn_status s) {
         case GDN_ERR_DTYPE: return "GDN_ERR_DTYPE: unsupported output dtype";
         case GDN_ERR_HIP: return "GDN_ERR_HIP: kernel launch failed";
         case GDN_ERR_ARG: return "GDN_ERR_ARG: invalid scalar argument";
+        case GDN_ERR_SCRATCH:
+            return "GDN_ERR_SCRATCH: the call needs more than the library's static scratch "
+                   "(GDN_SEQ_NOALLOC_MAX_BYTES per GPU)";
     }
     return "unknown gdn_status";
 }

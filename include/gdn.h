@@ -77,7 +77,9 @@ typedef enum gdn_status {
     GDN_ERR_ALIAS = 5,       /* state/out overlaps an input or each other; converter in-place */
     GDN_ERR_DTYPE = 6,       /* out_dtype is not GDN_F32 / GDN_BF16 (or not allowed here)     */
     GDN_ERR_HIP = 7,         /* the kernel launch failed; see gdn_last_hip_error()            */
-    GDN_ERR_ARG = 8          /* a scalar argument is invalid (eps negative or not finite)     */
+    GDN_ERR_ARG = 8,         /* a scalar argument is invalid (eps negative or not finite)     */
+    GDN_ERR_SCRATCH = 9      /* gdn_recurrence_seq_noalloc: the shape needs more scratch than
+                                GDN_SEQ_NOALLOC_MAX_BYTES                                      */
 } gdn_status;
 
 enum { GDN_F32 = 0, GDN_BF16 = 1 };
@@ -226,6 +228,46 @@ gdn_status gdn_recurrence_seq_ws(float *state, int64_t state_seq_stride,
  */
 int64_t gdn_seq_workspace_bytes(int32_t batch, int32_t seq_len, int32_t num_v_heads,
                                 int32_t k_dim, int32_t v_dim);
+
+/* Size of the static scratch array behind gdn_recurrence_seq_noalloc, per GPU. */
+#define GDN_SEQ_NOALLOC_MAX_BYTES (64ll << 20)
+
+/*
+ * gdn_recurrence_seq_noalloc -- for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  gdn_recurrence_seq_ws with the workspace taken from a static
+ * array inside the library instead of from the caller: same arguments as
+ * gdn_recurrence_seq, same kernels, results bit for bit equal to
+ * gdn_recurrence_seq_ws on the same inputs.  The call itself allocates nothing
+ * (no hipMalloc, no hipFree, no allocating library routine).
+ *   limit      the shape may need at most GDN_SEQ_NOALLOC_MAX_BYTES (64 MiB) of
+ *              workspace, gdn_seq_workspace_bytes(batch, seq_len, num_v_heads,
+ *              128, 128) -- e.g. batch * num_v_heads * ceil(seq_len / 16) <=
+ *              29127 records: one sequence of 48 heads up to 9696 tokens.  A
+ *              larger shape returns GDN_ERR_SCRATCH before anything is
+ *              launched.  Shapes that run without a workspace (another head
+ *              dim, very wide strides; see gdn_recurrence_seq_ws) need none.
+ *   set-up     The library holds one copy of the array per GPU for the life of
+ *              the process.  The first call on a device (with that device
+ *              current, as for any call: `stream` must belong to the current
+ *              device) resolves its address there with hipGetSymbolAddress;
+ *              make that first call outside graph capture.
+ *   sharing    Every call on one GPU uses that GPU's one array, and the array
+ *              keeps the last call's contents.  Calls that may overlap on one
+ *              GPU (two streams, two host threads) race on it and give wrong
+ *              results; order them on one stream.  Nothing in the array needs
+ *              to start at zero: each call writes every record it reads.
+ * Errors as gdn_recurrence_seq, plus GDN_ERR_SCRATCH.
+ */
+gdn_status gdn_recurrence_seq_noalloc(float *state, int64_t state_seq_stride,
+                                      const float *q, const float *k, int64_t qk_stride,
+                                      const float *v, int64_t v_stride,
+                                      const float *alpha, const float *beta, int64_t ab_stride,
+                                      const float *z, int64_t z_stride, const float *norm_weight,
+                                      float eps, float *out, int64_t out_stride,
+                                      int32_t batch, int32_t seq_len, int32_t num_k_heads,
+                                      int32_t num_v_heads, int32_t k_dim, int32_t v_dim,
+                                      void *stream);
 
 /*
  * gdn_decode_verify -- num_tokens (1..GDN_VERIFY_MAX_TOKENS) consecutive tokens

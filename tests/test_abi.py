@@ -33,7 +33,7 @@ def _declared():
 def test_header_declarations_found():
     names = _declared()
     assert "gdn_decode" in names and "gdn_decode_verify" in names
-    assert len(names) == 13, names
+    assert len(names) == 14, names
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -49,8 +49,9 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in range(9):
+    for code in range(10):
         assert lib.gdn_status_string(code)
+        assert b"unknown" not in lib.gdn_status_string(code).lower()
     assert b"unknown" in lib.gdn_status_string(99).lower()
 
 
@@ -194,6 +195,40 @@ def test_seq_ws_validation(lib):
     assert seq_ws(lib, T=0, ws=None) == 0                 # empty: no launch, OK
     assert seq_ws(lib, vs=NV * 128 - 4) == 3              # the plain call's checks come first
     assert seq_ws(lib, out=p["q"], ws=None) == 5
+
+
+def noalloc(lib, **kw):
+    """gdn_recurrence_seq_noalloc at D = 128 on fake bases 64 GiB apart, so that
+    long sequences fit between them."""
+    step, base = 1 << 36, 1 << 40
+    p = {n: base + i * step for i, n in enumerate(["state", "q", "k", "v", "alpha", "beta", "out"])}
+    d = 128
+    a = dict(state=p["state"], pitch=NV * d * d, q=p["q"], k=p["k"], qk=NK * d, v=p["v"],
+             vs=NV * d, al=p["alpha"], be=p["beta"], ab=NV, z=None, zs=0, gn=None, eps=1e-6,
+             out=p["out"], os=NV * d, B=1, T=5, nk=NK, nv=NV, dk=d, dv=d)
+    a.update(kw)
+    return lib.gdn_recurrence_seq_noalloc(a["state"], a["pitch"], a["q"], a["k"], a["qk"], a["v"],
+                                          a["vs"], a["al"], a["be"], a["ab"], a["z"], a["zs"],
+                                          a["gn"], a["eps"], a["out"], a["os"], a["B"], a["T"],
+                                          a["nk"], a["nv"], a["dk"], a["dv"], None)
+
+
+def test_noalloc_validation(lib):
+    import gated_deltanet_decode_delta_amd as gdn
+    limit = gdn.SEQ_NOALLOC_MAX_BYTES
+    assert limit == 64 << 20
+    # the largest length whose records fit, and the first that does not
+    chunks = limit // (NV * 2304)
+    assert lib.gdn_seq_workspace_bytes(1, 16 * chunks, NV, 128, 128) <= limit
+    assert lib.gdn_seq_workspace_bytes(1, 16 * chunks + 1, NV, 128, 128) > limit
+    assert noalloc(lib, T=16 * chunks + 1) == 9          # GDN_ERR_SCRATCH, nothing launched
+    assert noalloc(lib, B=3, T=16 * chunks) == 9
+    assert noalloc(lib, T=-1) == 2                       # the plain call's checks come first
+    assert noalloc(lib, T=0) == 0                        # empty: no launch, OK
+    assert noalloc(lib, vs=NV * 128 - 4, T=100) == 3
+    assert noalloc(lib, q=None) == 1
+    assert noalloc(lib, out=(1 << 40) + (1 << 36) + 64) == 5   # output over q
+    assert noalloc(lib, dk=96, dv=96) == 4
 
 
 def test_verify_validation(lib):
