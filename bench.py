@@ -127,21 +127,25 @@ def run_fp16(g, calls: int):
     st32 = torch.from_numpy(c.state).to(dev)
     st16 = g.gdn_state_f32_to_f16(st32)
     del st32
+    # consecutive calls rotate over three 403 MB pools (1.2 GB), so the state
+    # streams from HBM and not from the 256 MB Infinity Cache
+    pools = [st16] + [st16.clone() for _ in range(2)]
     t = {n: torch.from_numpy(getattr(c, n)).to(dev) for n in ("q", "k", "v", "z", "alpha", "beta", "gn")}
     out = torch.empty((B, NV * D), dtype=torch.bfloat16, device=dev)
 
     def step(i):
-        g.gdn_decode_f16state(st16, t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["z"], t["gn"],
-                              c.eps, out=out, num_k_heads=NK, num_v_heads=NV)
+        g.gdn_decode_f16state(pools[i % 3], t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["z"],
+                              t["gn"], c.eps, out=out, num_k_heads=NK, num_v_heads=NV)
 
     # 5 trials of `calls` calls each after a warmup; the median trial is the figure
     trials = sorted(_timed(step, calls, 5) for _ in range(5))
     ms = trials[2]
     state_bytes = 2.0 * B * NV * D * D * 2
     algo = B * NV * head_bytes(D, NV, NK, 2, 2, True)
-    del st16, t, out
+    del st16, pools, t, out
     torch.cuda.empty_cache()
-    return {"workload": "fp16 state decode, B=256, NV=48, NK=16, D=128, fused norm, bf16 out",
+    return {"workload": "fp16 state decode, B=256, NV=48, NK=16, D=128, fused norm, bf16 out, "
+                        "3 state pools in rotation",
             "ms_per_call": round(ms, 5), "trials": f"median of 5 trials x {calls} calls",
             "min_ms_per_call": round(trials[0], 5),
             "state_GBps": round(state_bytes / ms / 1e6, 1),
@@ -565,78 +569,257 @@ def pmc_traffic(algo_bytes: float):
     return pmc.get("bytes_per_launch")
 
 
+# rocprofv3 --pmc passes over one `--pmc-run` program (one pass per counter
+# set: a pass holds few counters of each hardware block, and the derived
+# counters need their own inputs)
+PMC_PASSES = (
+    ("fetch", "FETCH_SIZE"),
+    ("write", "WRITE_SIZE"),
+    ("insts", "SQ_INSTS_VALU SQ_WAVES SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT"),
+    ("busy", "VALUBusy OccupancyPercent MfmaUtil"),
+    ("l2", "TCC_HIT_sum TCC_MISS_sum"),
+)
+PMC_DETAIL_FILE = os.path.join(ROOT, "profiles", "kernel_counters.json")
+PMC_TABLE_FILE = os.path.join(ROOT, "profiles", "kernel_counters.md")
+
+
+def sources_hash() -> str:
+    """Hash of every library source (the counters of any kernel are void once
+    any of them changes)."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gated_deltanet_decode_delta_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def calibrate_and_profile(g, steps: int):
-    """Launch sequence for the counter runs: a plain device copy of a known size,
-    then the main step; rocprofv3 --pmc reports both per dispatch."""
+    """The program the counter passes run: a plain device copy of a known size
+    (to scale FETCH_SIZE / WRITE_SIZE), then `steps` calls of each profiled
+    workload, in this order: the B=64 fused-norm decode (8 rotated pools), the
+    B=256 binary16 decode, draft verify at T=2 then T=4 (B=64), the decode with
+    the fused input stage (two ring buffers, B=64) and the B=4, T=4096 sequence
+    through both entry points (raw o)."""
     import torch
+    from gated_deltanet_decode_delta_amd import inputs
+    dev = "cuda:0"
     n = 1 << 28
-    a = torch.empty(n, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
     b = torch.empty_like(a)
     for _ in range(3):
         b.copy_(a)
     torch.cuda.synchronize()
-    log(f"[bench] copy kernel: {n * 4} bytes read, {n * 4} bytes written per dispatch")
+    log(f"[pmc] copy kernel: {n * 4} bytes read, {n * 4} bytes written per dispatch")
     del a, b
-    run_main(g, steps, 2, 48)
+
+    def load(c, names):
+        return {x: torch.from_numpy(getattr(c, x)).to(dev) for x in names}
+
+    c = inputs.config_case("batched")
+    t = load(c, ("q", "k", "v", "z", "alpha", "beta", "gn"))
+    st = [torch.from_numpy(c.state).to(dev) for _ in range(8)]
+    out = torch.empty((c.B, c.NV * c.D), device=dev)
+    log("[pmc] decode B=64")
+    for i in range(steps):
+        g.gdn_decode_norm(st[i % 8], t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["z"], t["gn"],
+                          c.eps, out=out, num_k_heads=c.NK, num_v_heads=c.NV)
+    torch.cuda.synchronize()
+    del st, t, out
+
+    c = inputs.config_case("fp16_state")
+    t = load(c, ("q", "k", "v", "z", "alpha", "beta", "gn"))
+    st16 = g.gdn_state_f32_to_f16(torch.from_numpy(c.state).to(dev))
+    out = torch.empty((c.B, c.NV * c.D), dtype=torch.bfloat16, device=dev)
+    log("[pmc] binary16 decode B=256")
+    for i in range(steps):
+        g.gdn_decode_f16state(st16, t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["z"], t["gn"],
+                              c.eps, out=out, num_k_heads=c.NK, num_v_heads=c.NV)
+    torch.cuda.synchronize()
+    del st16, t, out
+
+    for T in (2, 4):
+        c = inputs.make_case(3100 + T, B=64, NK=16, NV=48, D=128, T=T, pitch=983040)
+        t = load(c, ("q", "k", "v", "z", "alpha", "beta", "gn"))
+        st = [torch.from_numpy(c.state).to(dev) for _ in range(4)]
+        inter = torch.empty((64 * (T - 1), 48 * 128 * 128), device=dev)
+        out = torch.empty((64 * T, 48 * 128), device=dev)
+        log(f"[pmc] verify B=64 T={T}")
+        for i in range(steps):
+            g.gdn_decode_verify(st[i % 4], t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["z"],
+                                t["gn"], c.eps, out=out, inter_state=inter, num_tokens=T,
+                                num_k_heads=16, num_v_heads=48)
+        torch.cuda.synchronize()
+        del st, t, inter, out
+
+    c = inputs.make_frontend_case(3200, B=64, NK=16, NV=48, D=128, taps=4, pitch=983040)
+    t = load(c, ("x", "w", "br", "ar", "dt", "rate", "z", "gn"))
+    st = [torch.from_numpy(c.state).to(dev) for _ in range(4)]
+    rings = [torch.from_numpy(c.ring).to(dev) for _ in range(2)]
+    out = torch.empty((64, 48 * 128), device=dev)
+    log("[pmc] fused input stage B=64, two ring buffers")
+    for i in range(steps):
+        g.gdn_decode_fused(st[i % 4], rings[i % 2], t["x"], t["w"], t["br"], t["ar"], t["dt"],
+                           t["rate"], t["z"], t["gn"], 1e-6, 1e-6, out=out,
+                           conv_state_out=rings[(i + 1) % 2], num_k_heads=16, num_v_heads=48)
+    torch.cuda.synchronize()
+    del st, rings, t, out
+
+    c = inputs.config_case("sequence")
+    t = load(c, ("q", "k", "v", "alpha", "beta"))
+    st = torch.from_numpy(c.state).to(dev)
+    out = torch.empty((c.B * c.T, c.NV * c.D), device=dev)
+    ws = torch.empty(g.gdn_seq_workspace_bytes(c.B, c.T, c.NV, c.D), dtype=torch.uint8, device=dev)
+    log("[pmc] sequence B=4 T=4096, with and without a workspace")
+    for i in range(max(1, steps // 4)):
+        g.gdn_recurrence_seq_ws(st, t["q"], t["k"], t["v"], t["alpha"], t["beta"], out=out,
+                                workspace=ws, seq_len=c.T, num_k_heads=c.NK, num_v_heads=c.NV,
+                                head_dim=c.D)
+        g.gdn_recurrence_seq(st, t["q"], t["k"], t["v"], t["alpha"], t["beta"], out=out,
+                             seq_len=c.T, num_k_heads=c.NK, num_v_heads=c.NV, head_dim=c.D)
+    torch.cuda.synchronize()
+    log("[pmc] done")
 
 
-def pmc_summarize(fetch_csv: str, write_csv: str):
-    """Turn the two rocprofv3 --pmc counter files of a --pmc-run (FETCH_SIZE,
-    then WRITE_SIZE, KiB per dispatch) into the committed traffic record: each
-    counter is scaled by what it reads for the 1 GiB device copy, whose bytes
-    are known."""
+def _pmc_rows(root: str):
+    """Every row of every rocprofv3 counter-collection csv under `root`."""
     import csv
-    import statistics
-
-    def per_kernel(path, counter):
-        vals = {}
+    import glob
+    rows = []
+    for path in sorted(glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True)):
         with open(path, newline="") as f:
-            for r in csv.DictReader(f):
-                if r["Counter_Name"] == counter:
-                    vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
-        return vals
+            rows.extend(csv.DictReader(f))
+    return rows
 
-    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
-    name = "void gdn::decode_kernel<128, float, 1, 16>(gdn::StepArgs)"
+
+def _algorithmic(kernel: str, n_dispatch: int):
+    """(label, algorithmic bytes per launch by dispatch index) of the profiled
+    decode-shaped kernels, from the figures the bench uses; None otherwise."""
+    hb = head_bytes
+    if "decode_kernel<128, float, 1, 16>" in kernel:
+        return "fused-norm decode, B=64", lambda i: 64 * 48 * hb(128, 48, 16, 4, 4, True)
+    if "decode_kernelILi128EDF16_Li2ELi32" in kernel or "decode_kernel<128, _Float16, 2, 32>" in kernel:
+        return "binary16 state, bf16 y, B=256", lambda i: 256 * 48 * hb(128, 48, 16, 2, 2, True)
+    if "verify_kernel<128, true>" in kernel:
+        def vb(i):   # the first half of the dispatches ran T = 2, the second T = 4
+            T = 2 if i < n_dispatch // 2 else 4
+            return 64 * (T + 1) * 48 * 128 * 128 * 4.0 + 64 * T * 48 * (hb(128, 48, 16, 4, 4, True)
+                                                                    - 2 * 128 * 128 * 4)
+        return "draft verify, B=64, T=2 then T=4", vb
+    if "fused_split_kernel<128, true>" in kernel:
+        C, taps = (2 * 16 + 48) * 128, 4
+        algo = (2.0 * 64 * 48 * 128 * 128 * 4 + 64 * (2 * taps - 1) * C * 4.0 + 64 * C * 4.0
+                + taps * C * 4.0 + 64 * 48 * (2 * 4 + 2 * 128 * 4) + 48 * 8.0)
+        return "fused input stage, two ring buffers, B=64", lambda i: algo
+    return None
+
+
+def pmc_summarize(root: str):
+    """Turn the counter passes of a --pmc-run (csv files under `root`, one
+    subdirectory per pass) into the committed records: per kernel the mean of
+    every counter per dispatch, HBM bytes scaled by what the counters read for
+    the 1 GiB device copy, and for the decode-shaped kernels the ratio of those
+    bytes to the algorithmic bytes.  Writes profiles/kernel_counters.json and
+    .md, and the main decode's traffic record (profiles/decode_norm_b64_pmc.json)."""
+    import statistics
+    rows = _pmc_rows(root)
+    per = {}   # kernel -> counter -> [values in dispatch order]
+    for r in sorted(rows, key=lambda r: int(r.get("Dispatch_Id") or 0)):
+        per.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(
+            float(r["Counter_Value"]))
     copy = "__amd_rocclr_copyBuffer"
     nbytes = float(1 << 30)
-    # the 1 GiB copy is the largest copy dispatch of the run (torch's set-up
-    # copies of the inputs use the same kernel on smaller buffers)
-    cf, cw = max(fetch[copy]), max(write[copy])
-    ff, wf = nbytes / (cf * 1024), nbytes / (cw * 1024)
-    kf, kw = statistics.mean(fetch[name]), statistics.mean(write[name])
-    from gated_deltanet_decode_delta_amd import inputs
-    cfg = inputs.CONFIGS["batched"]
-    algo = cfg["B"] * cfg["NV"] * head_bytes(cfg["D"], cfg["NV"], cfg["NK"], 4, 4, True)
+    ff = nbytes / (max(per[copy]["FETCH_SIZE"]) * 1024)
+    wf = nbytes / (max(per[copy]["WRITE_SIZE"]) * 1024)
+    out = {"sources_hash": sources_hash(), "kernel_hash": kernel_hash(),
+           "calibration": {"kernel": copy + " (torch copy_ of a 1 GiB fp32 buffer)",
+                           "fetch_factor": round(ff, 5), "write_factor": round(wf, 5)},
+           "passes": [p for p in PMC_PASSES], "kernels": {}}
+    for name, cs in per.items():
+        if not name.startswith("void gdn::") and not name.startswith("_ZN3gdn"):
+            continue
+        rec = {c: statistics.mean(v) for c, v in cs.items()}
+        rec["dispatches"] = max(len(v) for v in cs.values())
+        if "FETCH_SIZE" in cs and "WRITE_SIZE" in cs:
+            rec["hbm_bytes_per_launch"] = (rec["FETCH_SIZE"] * ff + rec["WRITE_SIZE"] * wf) * 1024
+        if "SQ_INSTS_VALU" in cs and "SQ_WAVES" in cs:
+            rec["valu_insts_per_wave"] = rec["SQ_INSTS_VALU"] / rec["SQ_WAVES"]
+        if "TCC_HIT_sum" in cs and "TCC_MISS_sum" in cs:
+            rec["l2_hit_pct"] = 100.0 * rec["TCC_HIT_sum"] / max(1.0, rec["TCC_HIT_sum"] + rec["TCC_MISS_sum"])
+        alg = _algorithmic(name, len(cs.get("FETCH_SIZE", [])))
+        if alg and "FETCH_SIZE" in cs and "WRITE_SIZE" in cs:
+            label, fn = alg
+            fe, wr = cs["FETCH_SIZE"], cs["WRITE_SIZE"]
+            ratios = [((fe[i] * ff + wr[i] * wf) * 1024) / fn(i) for i in range(min(len(fe), len(wr)))]
+            rec["workload"] = label
+            rec["traffic_over_algorithmic"] = statistics.mean(ratios)
+            rec["algorithmic_bytes_per_launch"] = [int(fn(0)), int(fn(len(fe) - 1))]
+        out["kernels"][name] = rec
+    with open(PMC_DETAIL_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+
+    main = next(k for k in out["kernels"] if "decode_kernel<128, float, 1, 16>" in k)
+    m = out["kernels"][main]
+    cfg = inputs_batched_algo()
     rec = {
-        "kernel": name,
+        "kernel": main,
         "workload": "gdn_decode_norm, B=64, NV=48, NK=16, D=128, fp32 state, pitch 983040, fp32 out",
         "kernel_hash": kernel_hash(),
         "kernel_sources": list(KERNEL_SOURCES),
-        "dispatches": min(len(fetch[name]), len(write[name])),
-        "fetch_size_kib_per_dispatch": round(kf, 1),
-        "write_size_kib_per_dispatch": round(kw, 1),
-        "calibration": {"kernel": copy + " (torch copy_ of a 1 GiB fp32 buffer)",
-                        "bytes_read": int(nbytes), "bytes_written": int(nbytes),
-                        "fetch_size_kib": round(cf, 1), "write_size_kib": round(cw, 1),
-                        "fetch_factor": round(ff, 5), "write_factor": round(wf, 5)},
-        "fetch_bytes_per_launch": int(kf * 1024 * ff),
-        "write_bytes_per_launch": int(kw * 1024 * wf),
-        "bytes_per_launch": int(kf * 1024 * ff + kw * 1024 * wf),
-        "algorithmic_bytes_per_launch": int(algo),
-        "commands": [
-            "cd /tmp && TMPDIR=/tmp timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE -d <out>/fetch -o fetch "
-            "--output-format csv -- python3 <repo>/bench.py --pmc-run --steps 20",
-            "cd /tmp && TMPDIR=/tmp timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE -d <out>/write -o write "
-            "--output-format csv -- python3 <repo>/bench.py --pmc-run --steps 20",
-            "python3 <repo>/bench.py --pmc-summarize <out>/fetch/fetch_counter_collection.csv "
-            "<out>/write/write_counter_collection.csv"],
+        "dispatches": m["dispatches"],
+        "fetch_size_kib_per_dispatch": round(m["FETCH_SIZE"], 1),
+        "write_size_kib_per_dispatch": round(m["WRITE_SIZE"], 1),
+        "calibration": out["calibration"],
+        "fetch_bytes_per_launch": int(m["FETCH_SIZE"] * 1024 * ff),
+        "write_bytes_per_launch": int(m["WRITE_SIZE"] * 1024 * wf),
+        "bytes_per_launch": int(m["hbm_bytes_per_launch"]),
+        "algorithmic_bytes_per_launch": int(cfg),
+        "commands": pmc_commands(),
     }
     with open(PMC_FILE, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
-    print(json.dumps({"bytes_per_launch": rec["bytes_per_launch"],
-                      "algorithmic": rec["algorithmic_bytes_per_launch"]}))
+
+    def fmt(x, nd=1):
+        return "" if x is None else (f"{x:,.{nd}f}" if isinstance(x, float) else f"{x:,}")
+
+    lines = ["# Counters per kernel -- decode-shaped kernels and the sequence passes", "",
+             "Every figure is the mean per dispatch of a rocprofv3 `--pmc` pass over "
+             "`bench.py --pmc-run` (the workloads and their order are in `calibrate_and_profile`); "
+             "HBM bytes are FETCH_SIZE and WRITE_SIZE scaled by what the same counters read for a "
+             f"1 GiB device copy (factors {ff:.5f} and {wf:.5f}).", "",
+             f"Library sources hash `{out['sources_hash']}`.", "", "Commands (repo at `<repo>`, "
+             "output under `<out>`):", "", "```"] + pmc_commands() + ["```", "",
+             "| Kernel | Workload | Dispatches | HBM bytes / launch | / algorithmic | VALU insts / wave "
+             "| VALUBusy % | Occupancy % | MfmaUtil % | L2 hit % | LDS bank conflicts / LDS insts |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for name, r in sorted(out["kernels"].items()):
+        conf = (r["SQ_LDS_BANK_CONFLICT"] / r["SQ_INSTS_LDS"]) if r.get("SQ_INSTS_LDS") else None
+        lines.append("| `{}` | {} | {} | {} | {} | {} | {} | {} | {} | {} | {} |".format(
+            name.replace("void ", "").replace("(gdn::StepArgs)", ""), r.get("workload", ""),
+            r["dispatches"], fmt(r.get("hbm_bytes_per_launch"), 0),
+            fmt(r.get("traffic_over_algorithmic"), 4), fmt(r.get("valu_insts_per_wave")),
+            fmt(r.get("VALUBusy")), fmt(r.get("OccupancyPercent")), fmt(r.get("MfmaUtil")),
+            fmt(r.get("l2_hit_pct")), fmt(conf, 3)))
+    with open(PMC_TABLE_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps({"kernels": len(out["kernels"]), "main_bytes_per_launch": rec["bytes_per_launch"],
+                      "main_algorithmic": rec["algorithmic_bytes_per_launch"]}))
+
+
+def inputs_batched_algo() -> float:
+    from gated_deltanet_decode_delta_amd import inputs
+    cfg = inputs.CONFIGS["batched"]
+    return cfg["B"] * cfg["NV"] * head_bytes(cfg["D"], cfg["NV"], cfg["NK"], 4, 4, True)
+
+
+def pmc_commands():
+    cmds = [f"cd /tmp && TMPDIR=/tmp timeout -s KILL 300 rocprofv3 --pmc {ctr} -d <out>/{name} -o {name} "
+            f"--output-format csv -- python3 <repo>/bench.py --pmc-run --steps 12"
+            for name, ctr in PMC_PASSES]
+    return cmds + ["python3 <repo>/bench.py --pmc-summarize <out>"]
 
 
 def main():
@@ -652,14 +835,14 @@ def main():
                          "fused, real_head")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--seq-only", action="store_true", help="time the sequence workload alone")
-    ap.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="write the traffic record from two rocprofv3 --pmc counter files (no GPU)")
+    ap.add_argument("--pmc-summarize", metavar="DIR",
+                    help="write the counter records from the rocprofv3 --pmc passes under DIR (no GPU)")
     ap.add_argument("--pmc-run", action="store_true",
-                    help="copy-kernel calibration + main step only (for rocprofv3 --pmc)")
+                    help="copy-kernel calibration + the profiled workloads (for rocprofv3 --pmc)")
     args = ap.parse_args()
 
     if args.pmc_summarize:
-        pmc_summarize(*args.pmc_summarize)
+        pmc_summarize(args.pmc_summarize)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -42,7 +42,7 @@ fused_kernel(StepArgs a, FrontArgs f) {
     float *gal = lds + (2 + R) * D;    // [R] decay
     float *gbe = gal + R;              // [R] write strength
     float *den = gbe + R;              // [2] L2 denominators of q_g and k_g
-    __shared__ float part[2][TL::NGA];
+    __shared__ float part[2][TL::NT / 64];   // per-wave sums of o^2, by head parity
 
     const int wg = blockIdx.x;
     const int b = wg / a.nk;
@@ -210,12 +210,13 @@ fused_kernel(StepArgs a, FrontArgs f) {
         } else {
             // one barrier per head; the partials alternate between two buffers so
             // that head m + 2 never overwrites what a slow thread still reads
-            if (active && p == 0) part[m & 1][grp] = sumsq;
+            const float wsum = wave_groups_sum<LPR>(active ? sumsq : 0.f);
+            if ((tid & 63) == 0) part[m & 1][tid >> 6] = wsum;
             __syncthreads();
             if (active && p < RPL) {
                 float tot = 0.f;
 #pragma unroll
-                for (int i = 0; i < TL::NGA; ++i) tot += part[m & 1][i];
+                for (int i = 0; i < TL::NT / 64; ++i) tot += part[m & 1][i];
                 const float r = sqrtf(tot * (1.0f / D) + a.eps);
                 outp[orow] = (gr * o_mine / r) * silu(zr);
             }
@@ -243,7 +244,7 @@ fused_split_kernel(StepArgs a, FrontArgs f, float *ring_out) {
 
     __shared__ __align__(16) float feat[3 * D];   // q_g, k_g, v_h
     __shared__ float gates[2], den[2];
-    __shared__ float part[TL::NGA];
+    __shared__ float part[TL::NT / 64];      // per-wave sums of o^2
 
     const int wg = blockIdx.x;
     const int b = wg / a.nv;
@@ -401,12 +402,13 @@ fused_split_kernel(StepArgs a, FrontArgs f, float *ring_out) {
     if constexpr (!NORM) {
         if (active && p < RPL) outp[orow] = o_mine;
     } else {
-        if (active && p == 0) part[grp] = sumsq;
+        const float wsum = wave_groups_sum<LPR>(active ? sumsq : 0.f);
+        if ((tid & 63) == 0) part[tid >> 6] = wsum;
         __syncthreads();
         if (active && p < RPL) {
             float tot = 0.f;
 #pragma unroll
-            for (int i = 0; i < TL::NGA; ++i) tot += part[i];
+            for (int i = 0; i < TL::NT / 64; ++i) tot += part[i];
             const float r = sqrtf(tot * (1.0f / D) + a.eps);
             outp[orow] = (gr * o_mine / r) * silu(zr);
         }

@@ -42,4 +42,26 @@ struct DecodeTile {
     static_assert(NGA <= NG, "rows fit the workgroup");
 };
 
+// Non-temporal store of a state vector (8 or 16 bytes).  The vector goes out as
+// 32-bit words: hipcc drops the non-temporal hint of the decode's store of a
+// vector of binary16 values (it emits a plain store), but keeps it on words.
+template <typename V>
+__device__ __forceinline__ void store_state_nt(const V &x, V *p) {
+    typedef uint32_t U __attribute__((ext_vector_type(sizeof(V) / 4)));
+    static_assert(sizeof(V) % 4 == 0 && sizeof(V) == sizeof(U), "whole 32-bit words");
+    __builtin_nontemporal_store(__builtin_bit_cast(U, x), reinterpret_cast<U *>(p));
+}
+
+// Sum over a whole wave of per-row-group values, where the LPR lanes of each
+// group hold the same value: a butterfly over lane distances LPR, 2 LPR, ..., 32
+// (ds_bpermute).  Every lane ends with the same bits (each step adds a pair in
+// either order, and IEEE addition commutes), so the result is deterministic.
+// Call with the whole wave active.
+template <int LPR>
+__device__ __forceinline__ float wave_groups_sum(float x) {
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
 }  // namespace gdn

@@ -21,33 +21,52 @@ def test_head_bytes_match_the_stated_per_launch_figures():
 
 
 def _counter_csv(path, counter, rows):
+    path.parent.mkdir(parents=True, exist_ok=True)
     with open(path, "w") as f:
-        f.write("Kernel_Name,Counter_Name,Counter_Value\n")
-        for name, value in rows:
-            f.write(f'"{name}",{counter},{value}\n')
+        f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+        for i, (name, value) in enumerate(rows):
+            f.write(f'{i + 1},"{name}",{counter},{value}\n')
 
 
 def test_pmc_record_scaling_and_hash_gate(tmp_path, monkeypatch):
     kernel = "void gdn::decode_kernel<128, float, 1, 16>(gdn::StepArgs)"
+    verify = "void gdn::verify_kernel<128, true>(gdn::StepArgs, float*, long)"
     copy = "__amd_rocclr_copyBuffer"
-    fetch, write = tmp_path / "fetch.csv", tmp_path / "write.csv"
+    root = tmp_path / "passes"
     # the 1 GiB copy reads 512 Ki KiB of FETCH_SIZE (factor 2) and writes
     # 1 Mi KiB of WRITE_SIZE (factor 1); a smaller copy must not be taken
-    _counter_csv(fetch, "FETCH_SIZE", [(copy, 1000.0), (copy, 524288.0), (kernel, 100000.0),
-                                       (kernel, 100002.0)])
-    _counter_csv(write, "WRITE_SIZE", [(copy, 2000.0), (copy, 1048576.0), (kernel, 200000.0),
-                                       (kernel, 200000.0)])
+    _counter_csv(root / "fetch" / "fetch_counter_collection.csv", "FETCH_SIZE",
+                 [(copy, 1000.0), (copy, 524288.0), (kernel, 100000.0), (kernel, 100002.0),
+                  (verify, 1000.0), (verify, 1000.0), (verify, 3000.0), (verify, 3000.0)])
+    _counter_csv(root / "write" / "write_counter_collection.csv", "WRITE_SIZE",
+                 [(copy, 2000.0), (copy, 1048576.0), (kernel, 200000.0), (kernel, 200000.0),
+                  (verify, 0.0), (verify, 0.0), (verify, 0.0), (verify, 0.0)])
+    _counter_csv(root / "insts" / "insts_counter_collection.csv", "SQ_WAVES",
+                 [(kernel, 49152.0), (kernel, 49152.0)])
+    _counter_csv(root / "insts2" / "insts2_counter_collection.csv", "SQ_INSTS_VALU",
+                 [(kernel, 49152.0 * 240), (kernel, 49152.0 * 240)])
     out = tmp_path / "pmc.json"
     monkeypatch.setattr(bench, "PMC_FILE", str(out))
-    bench.pmc_summarize(str(fetch), str(write))
+    monkeypatch.setattr(bench, "PMC_DETAIL_FILE", str(tmp_path / "detail.json"))
+    monkeypatch.setattr(bench, "PMC_TABLE_FILE", str(tmp_path / "table.md"))
+    bench.pmc_summarize(str(root))
     rec = json.loads(out.read_text())
     assert rec["calibration"]["fetch_factor"] == pytest.approx(2.0)
     assert rec["calibration"]["write_factor"] == pytest.approx(1.0)
     assert rec["fetch_bytes_per_launch"] == int(100001.0 * 1024 * 2)
     assert rec["write_bytes_per_launch"] == int(200000.0 * 1024)
-    assert rec["bytes_per_launch"] == rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+    assert abs(rec["bytes_per_launch"] - rec["fetch_bytes_per_launch"] - rec["write_bytes_per_launch"]) <= 1
     assert rec["kernel_hash"] == bench.kernel_hash()
     assert bench.pmc_traffic(408_444_928) == rec["bytes_per_launch"]
+    detail = json.loads((tmp_path / "detail.json").read_text())["kernels"]
+    assert detail[kernel]["valu_insts_per_wave"] == pytest.approx(240.0)
+    # verify: the first half of its dispatches is T = 2, the second T = 4
+    v = detail[verify]
+    t2 = 64 * 3 * 48 * 128 * 128 * 4.0 + 64 * 2 * 48 * (bench.head_bytes(128, 48, 16, 4, 4, True)
+                                                          - 2 * 128 * 128 * 4)
+    assert v["algorithmic_bytes_per_launch"][0] == int(t2)
+    assert v["algorithmic_bytes_per_launch"][1] > v["algorithmic_bytes_per_launch"][0]
+    assert "verify_kernel" in (tmp_path / "table.md").read_text()
     # a record taken on other kernel sources is not reported
     rec["kernel_hash"] = "0" * 16
     out.write_text(json.dumps(rec))
