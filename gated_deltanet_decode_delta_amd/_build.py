@@ -27,10 +27,11 @@ FLAGS = [
 ]
 
 
-# Per-source extra flags.  The split sequence kernel keeps its matrix-core
+# Per-source extra flags.  The split and grouped sequence kernels keep their matrix-core
 # accumulators in ordinary VGPRs: left to itself the compiler puts them in
 # AGPRs and copies every one back for the vector-ALU work on it.
-EXTRA = {"gdn_seq_split.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"gdn_seq_split.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "gdn_seq_group.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def sources():

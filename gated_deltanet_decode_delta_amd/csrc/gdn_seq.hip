@@ -353,8 +353,11 @@ static hipError_t by_dim(const StepArgs &a, int dim, hipStream_t stream) {
 
 hipError_t launch_seq(const StepArgs &a, int dim, OutMode mode, hipStream_t stream) {
     // D = 128 (every head shape of the Qwen3.5/3.8 family) runs chunked on the
-    // matrix cores; the other head dims use the register-resident token loop
-    if (dim == 128) return launch_seq_mfma(a, mode, stream);
+    // matrix cores, a workgroup per key-head quarter where the shape allows it,
+    // else a workgroup per head; the other head dims use the register-resident
+    // token loop
+    if (dim == 128) return seq_group_fits(a) ? launch_seq_group(a, mode, stream)
+                                             : launch_seq_mfma(a, mode, stream);
     if (mode == kOutRawF32) return by_dim<false>(a, dim, stream);
     if (mode == kOutNormF32) return by_dim<true>(a, dim, stream);
     return hipErrorInvalidValue;

@@ -1,0 +1,459 @@
+// gdn_seq_group.hip -- the T-token recurrence at D = 128 without a workspace:
+// every workgroup forms the chunk quantities it needs itself, for all value
+// heads of one key head, and holds one quarter of their state rows.
+//
+// Same chunked algebra as gdn_seq_mfma.hip and gdn_seq_split.hip (16 tokens per
+// chunk; metrale "layers/ops/ssm_gdn_a.rs" `gdn_prefill_regresident` for the
+// operation, the update of logicaffeine "codegen_cuda/gdn.rs" `gdn_step`): with
+// M[t][s] = alpha_{s+1} ... alpha_t, P_t = alpha_0 ... alpha_t and S0 the state
+// at the chunk start,
+//     C' = T R,  R = beta (V - P S0 K^T),  T = (I + A)^{-1},
+//          A[t][s] = beta_t M[t][s] (k_s.k_t)  (s < t)
+//     O  = P S0 Q^T + C' G^T,  G[t][s] = M[t][s] (k_s.q_t)  (s <= t)
+//     S_end = P_15 S0 + C' diag(M[15][.]) K.
+//
+// Mapping.  With the tiled pairing the value heads of key head g are g, g + NK,
+// ..., g + (R - 1) NK (R = NV / NK), and they all read the same k and q.  One
+// workgroup takes (sequence, key head, quarter): rows 32 quarter .. +31 of each
+// of those R heads, four waves per head laid out as in the workspace path's
+// state pass (wave (strip, half) owns 16 rows x 64 key columns, four 16x16
+// accumulator tiles), 4 R waves in all.  The chunk's k and q are staged once for
+// the R heads, and its k.k / k.q tiles are formed once for them, so forming T
+// and G in the workgroup costs 64 extra matrix-core products per chunk per
+// workgroup (on 12 R-independent product streams of 52) and one triangular
+// solve for the R heads side by side (lane group g solves head g).  At the real
+// shape (B = 4, NK = 16, R = 3) that is 256 workgroups of 12 waves, one per CU,
+// three waves per SIMD, against 192 workgroups of eight waves for the kernel
+// that gives each head one workgroup.
+//
+// The chunk-level work runs ahead of the state work.  During chunk c (two
+// workgroup barriers):
+//   before the first: U / W products (every wave); chunk c + 2 staged
+//     (k, q, alpha, beta); then A, T and G of chunk c (wave 0, after its own
+//     products);
+//   between them: the strip chains (R, C' in half 0; the first term of O in
+//     half 1) and nothing else, since every wave waits on this short phase
+//     (chunk work placed there on the half-1 waves made the kernel 20% slower);
+//   after the second: O and its stores, the state update; chunk c + 2's k.k /
+//     k.q partial tiles (waves 1..3) and range products M, P, D (one wave per
+//     SIMD); the loads of chunk c + 3's k, q, alpha, beta and chunk c + 1's v.
+#include "gdn_chunk.h"
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+using namespace chunk;
+
+namespace {
+
+constexpr int kBufs = 3;        // k, q, alpha, beta, P, D: chunks c, c + 1, c + 2
+
+}  // namespace
+
+template <int R>
+__global__ void __launch_bounds__(256 * R) seq_group_kernel(StepArgs a, int nc) {
+    constexpr int NT = 256 * R;
+    constexpr int NW = 4 * R;
+    constexpr int KQP = (512 + NT - 1) / NT;   // 16-byte pieces of a chunk's k (and of q) per thread
+    constexpr int kParts = 3;                   // partial k.k / k.q tiles (waves 1..3)
+    __shared__ __align__(16) float kq_s[kBufs][2][kC * kKS];   // [chunk % 3][k, q] rows of a chunk
+    __shared__ __align__(16) float ab_s[kBufs][2][R][kC];      // [chunk % 3][alpha, beta][head]
+    __shared__ __align__(16) float pd_s[kBufs][2][R][kC];      // [chunk % 3][P, D][head]
+    __shared__ f32x4 part_s[2][kParts][2][64];                 // [chunk & 1][part][k.k, k.q]
+    __shared__ __align__(16) float m_s[2][R][kC * kTS];        // [chunk & 1] M[t][s]
+    __shared__ __align__(16) float mt_s[2][R][kC * kTS];       // [chunk & 1] M^T
+    __shared__ __align__(16) float t_s[2][R][kC * kTS];        // [chunk & 1] T row-major
+    __shared__ __align__(16) float g_s[2][R][kC * kTS];        // [chunk & 1] G / sqrt(D) row-major
+    __shared__ __align__(16) float a_s[R][kC * kTS];           // a_s[s][t] = A[t][s] of the chunk solved
+    __shared__ f32x4 x_s[NW][64];                              // each wave's partial its partner needs
+    __shared__ f32x4 c_s[2 * R][64];                           // C' of each strip
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l = tid & 63, g = l >> 4, li = l & 15;
+    const int m = w >> 2;                    // value head m of the key head
+    const int half = w & 1, strip = (w >> 1) & 1;
+
+    // Block -> (sequence, key head, quarter): the four quarters of a key head get
+    // indices equal modulo 8, so they run on one XCD and share its L2 for the
+    // key head's k and q rows.
+    const int ngroups = a.batch * a.nk;
+    const int full = ngroups / 8 * 8;
+    int grp, quarter;
+    {
+        const int bid = blockIdx.x;
+        if (bid < full * 4) {
+            const int r = bid & 31;
+            grp = (bid >> 5) * 8 + (r & 7);
+            quarter = r >> 3;
+        } else {
+            const int r = bid - full * 4, rem = ngroups - full;
+            grp = full + r % rem;
+            quarter = r / rem;
+        }
+    }
+    const int b = grp / a.nk;
+    const int kh = grp - b * a.nk;
+    const int h = kh + m * a.nk;             // tiled pairing
+    const int T = a.seq_len;
+    const int64_t row_base = (int64_t)b * T;
+    const int row = 32 * quarter + 16 * strip + li;          // state row (value index) of head h
+    float *srow = static_cast<float *>(a.state) + (int64_t)b * a.pitch + (int64_t)h * (kD * kD) +
+                  (int64_t)row * kD + 64 * half + 4 * g;
+
+    // The true state is gam * S; S[t4][r] = S[row][64 half + 16 t4 + 4 g + r].
+    f32x4 S[4];
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) S[t4] = *reinterpret_cast<const f32x4 *>(srow + 16 * t4);
+    float gam = 1.0f;
+
+    // k and q of a chunk: pieces f = tid + NT u < 512, token f >> 5, columns
+    // (f % 32) * 4, through descriptors based at the chunk's first row (rows past
+    // T read 0); alpha and beta of head e >> 4, token e % 16 for thread e < 16 R
+    // (alpha 1, beta 0 past T: such tokens change nothing).
+    const int64_t kq0 = row_base * a.qk_stride + (int64_t)kh * kD;
+    int kq_off[KQP];
+#pragma unroll
+    for (int u = 0; u < KQP; ++u) {
+        const int f = tid + NT * u;
+        kq_off[u] = (int)((((f & 511) >> 5) * a.qk_stride + (f & 31) * 4) * 4);
+    }
+    f32x4 pk[KQP], pq[KQP];
+    float pal = 1.0f, pbe = 0.0f;
+    const bool ab_thread = tid < 16 * R;
+    const int64_t ab_col = kh + (int64_t)(tid >> 4) * a.nk;
+    auto prefetch = [&](int c) {
+        const int t0 = c * kC;
+        const int64_t off = kq0 + (int64_t)t0 * a.qk_stride;   // uniform
+        const int64_t nb = (int64_t)(T - t0) * a.qk_stride * 4;
+        const __amdgpu_buffer_rsrc_t rk = buf_rsrc(a.k + off, nb), rq = buf_rsrc(a.q + off, nb);
+#pragma unroll
+        for (int u = 0; u < KQP; ++u) {
+            if (tid + NT * u < 512) {
+                pk[u] = buf_load4(rk, kq_off[u]);
+                pq[u] = buf_load4(rq, kq_off[u]);
+            }
+        }
+        pal = 1.0f;
+        pbe = 0.0f;
+        if (ab_thread && t0 + (tid & 15) < T) {
+            const int64_t rr = (row_base + t0 + (tid & 15)) * a.ab_stride + ab_col;
+            pal = a.alpha[rr];
+            pbe = a.beta[rr];
+        }
+    };
+    auto stage = [&](int c) {
+        const int b3 = c % kBufs;
+#pragma unroll
+        for (int u = 0; u < KQP; ++u) {
+            const int f = tid + NT * u;
+            if (f < 512) {
+                *reinterpret_cast<f32x4 *>(&kq_s[b3][0][(f >> 5) * kKS + (f & 31) * 4]) = pk[u];
+                *reinterpret_cast<f32x4 *>(&kq_s[b3][1][(f >> 5) * kKS + (f & 31) * 4]) = pq[u];
+            }
+        }
+        if (ab_thread) {
+            ab_s[b3][0][tid >> 4][tid & 15] = pal;
+            ab_s[b3][1][tid >> 4][tid & 15] = pbe;
+        }
+    };
+
+    // The chunk-level work of chunk c + 2 runs after the second barrier of chunk
+    // c, spread so that each SIMD ends up with about the same matrix-core and
+    // vector-ALU time: the half-1 waves (SIMDs 1, 3) carry four more products
+    // each than the half-0 waves (SIMDs 0, 2), and wave 0 (SIMD 0) the solve.
+    //
+    // Range products, by the four waves of one head slot (waves 4..7, or 0..3
+    // when R = 1, one per SIMD): wave rw takes rows t = 4 rw + g of every head,
+    // lane li the column s.  With x_s = alpha_{s+1} for s < t (else 1), M[t][s]
+    // is the suffix product x_s ... x_15 along the 16-lane row (no division, so
+    // any alpha >= 0 is exact to fp32 rounding).  Also P_t = alpha_0 M[t][0]
+    // and D[s] = M[15][s].
+    constexpr int kRangeW0 = R > 1 ? 4 : 0;
+    auto range_products = [&](int c) {
+        if (w >= kRangeW0 && w < kRangeW0 + 4) {
+            const int b3 = c % kBufs, par = c & 1;
+            const int t = 4 * (w - kRangeW0) + g, s = li;
+#pragma unroll
+            for (int hm = 0; hm < R; ++hm) {
+                float x = ab_s[b3][0][hm][s < t ? s + 1 : 0];   // index kept inside the row
+                x = s < t ? x : 1.0f;
+                x *= dpp_from_above<1>(x);
+                x *= dpp_from_above<2>(x);
+                x *= dpp_from_above<4>(x);
+                x *= dpp_from_above<8>(x);
+                const float v = t >= s ? x : 0.0f;
+                m_s[par][hm][t * kTS + s] = v;
+                mt_s[par][hm][s * kTS + t] = v;
+                if (t == kC - 1) pd_s[b3][1][hm][s] = v;
+                if (s == 0) pd_s[b3][0][hm][t] = ab_s[b3][0][hm][0] * v;
+            }
+        }
+    };
+
+    // k.k and k.q tiles in three parts over the 16-column slices: wave 2
+    // (SIMD 2) slices 0..3, wave 1 (SIMD 1) slices 4, 5, wave 3 (SIMD 3) slices
+    // 6, 7.  Lane (g, li), register r holds k_{4g+r}.k_{li} and k_{4g+r}.q_{li};
+    // the parts are summed where they are used.
+    auto tiles = [&](int c) {
+        if (w >= 1 && w <= 3) {
+            const int b3 = c % kBufs, par = c & 1;
+            const int part = w - 1, s0 = w == 2 ? 0 : (w == 1 ? 4 : 6), ns = w == 2 ? 4 : 2;
+            f32x4 KK = f32x4{0.f, 0.f, 0.f, 0.f}, KQ = KK;
+            for (int sl = s0; sl < s0 + ns; ++sl) {
+                const f32x4 ka = *reinterpret_cast<const f32x4 *>(&kq_s[b3][0][li * kKS + 16 * sl + 4 * g]);
+                const f32x4 qa = *reinterpret_cast<const f32x4 *>(&kq_s[b3][1][li * kKS + 16 * sl + 4 * g]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    KK = mfma(ka[r], ka[r], KK);
+                    KQ = mfma(ka[r], qa[r], KQ);
+                }
+            }
+            part_s[par][part][0][l] = KK;
+            part_s[par][part][1][l] = KQ;
+        }
+    };
+
+    // Wave 0: A, T and G of chunk c for the R heads.  Lane (g, li) owns
+    // A[4g + r][li] = beta_{4g+r} M[4g+r][li] (k_{4g+r}.k_{li}) below the
+    // diagonal and G[li][4g + r] = M[li][4g+r] (k_{4g+r}.q_{li}) / sqrt(D); k.k is
+    // symmetric, so no value moves between lanes before LDS.  Then lane group g
+    // solves head g: T = (I + A)^{-1} column li by column-oriented forward
+    // substitution with the identity column as right-hand side (the entries
+    // above li come out exactly 0 and T[li][li] exactly 1).
+    auto solve = [&](int c) {
+        if (w == 0) {
+            const int b3 = c % kBufs, par = c & 1;
+            f32x4 KK = part_s[par][0][0][l], KQ = part_s[par][0][1][l];
+#pragma unroll
+            for (int v2 = 1; v2 < kParts; ++v2) {
+                KK += part_s[par][v2][0][l];
+                KQ += part_s[par][v2][1][l];
+            }
+            const f32x4 KQs = KQ * a.scale;
+#pragma unroll
+            for (int hm = 0; hm < R; ++hm) {
+                const f32x4 bet = *reinterpret_cast<const f32x4 *>(&ab_s[b3][1][hm][4 * g]);
+                const f32x4 mA = *reinterpret_cast<const f32x4 *>(&mt_s[par][hm][li * kTS + 4 * g]);  // M[4g+r][li]
+                const f32x4 mG = *reinterpret_cast<const f32x4 *>(&m_s[par][hm][li * kTS + 4 * g]);   // M[li][4g+r]
+                f32x4 acol;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acol[r] = li < 4 * g + r ? bet[r] * mA[r] * KK[r] : 0.0f;
+                *reinterpret_cast<f32x4 *>(&a_s[hm][li * kTS + 4 * g]) = acol;
+                *reinterpret_cast<f32x4 *>(&g_s[par][hm][li * kTS + 4 * g]) = mG * KQs;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            const int hs = g < R ? g : R - 1;   // lane groups past R repeat the last head, unwritten
+            // the identity column is formed here, not hoisted out of the chunk
+            // loop (16 registers held across it)
+            float one = 1.0f;
+            asm volatile("" : "+v"(one));
+            float x[kC];
+#pragma unroll
+            for (int t = 0; t < kC; ++t) x[t] = t == li ? one : 0.0f;
+#pragma unroll
+            for (int s2 = 0; s2 < kC - 1; ++s2) {
+#pragma unroll
+                for (int t4 = (s2 + 1) / 4; t4 < kC / 4; ++t4) {
+                    const f32x4 av = *reinterpret_cast<const f32x4 *>(&a_s[hs][s2 * kTS + 4 * t4]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (4 * t4 + e > s2) x[4 * t4 + e] = fmaf(-av[e], x[s2], x[4 * t4 + e]);
+                }
+            }
+            if (g < R) {
+#pragma unroll
+                for (int t = 0; t < kC; ++t) t_s[par][g][t * kTS + li] = x[t];
+            }
+        }
+    };
+
+    // v of the lane's row for tokens 4g .. 4g+3 (half 0 only; rows past T read 0)
+    const int64_t v0 = row_base * a.v_stride + (int64_t)h * kD;
+    const int v_off = (int)((4 * g * a.v_stride + row) * 4);
+    const int v_step = (int)(a.v_stride * 4);
+    float vv[4];
+    auto load_v = [&](int c) {
+        const int t0 = c * kC;
+        const __amdgpu_buffer_rsrc_t rv =
+            buf_rsrc(a.v + v0 + (int64_t)t0 * a.v_stride, (int64_t)(T - t0) * a.v_stride * 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            vv[r] = 0.0f;
+            if (half == 0) vv[r] = buf_load1(rv, v_off + r * v_step);
+        }
+    };
+
+    // Prologue: chunks 0 and 1 staged, their range products and tiles formed;
+    // chunk 2's loads and chunk 0's v in flight.
+    prefetch(0);
+    __builtin_amdgcn_s_waitcnt(0);
+    stage(0);
+    if (nc > 1) {
+        prefetch(1);
+        __builtin_amdgcn_s_waitcnt(0);
+        stage(1);
+    }
+    __syncthreads();
+    range_products(0);
+    tiles(0);
+    if (nc > 1) {
+        range_products(1);
+        tiles(1);
+    }
+    if (nc > 2) prefetch(2);
+    load_v(0);
+    // drain every load (the state included) so that no conservative vmcnt wait
+    // lands inside the chunk loop
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    const float *o0 = static_cast<const float *>(a.out) + row_base * a.out_stride + (int64_t)h * kD;
+    const int o_off = (int)((4 * g * a.out_stride + row) * 4);
+    const int o_step = (int)(a.out_stride * 4);
+    for (int c = 0; c < nc; ++c) {
+        const int b3 = c % kBufs, par = c & 1;
+        const int t0 = c * kC;
+        // the update's k operands (token 4g + s4, column 64 half + 16 t4 + li),
+        // requested now so that their LDS latency is long past at the update
+        float kcv[16];
+        {
+            const float *kc = &kq_s[b3][0][4 * g * kKS + 64 * half + li];
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+                for (int t4 = 0; t4 < 4; ++t4) kcv[4 * s4 + t4] = kc[s4 * kKS + 16 * t4];
+        }
+        // partial U^T = K S^T and W^T = Q S^T over this wave's 64 columns: Mp is
+        // the one the wave goes on with (U in half 0, W in half 1), Xp the one
+        // its partner needs
+        f32x4 Mp = f32x4{0.f, 0.f, 0.f, 0.f}, Xp = Mp;
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) {
+            const int col = 64 * half + 16 * t4 + 4 * g;
+            const f32x4 ma = *reinterpret_cast<const f32x4 *>(&kq_s[b3][half][li * kKS + col]);
+            const f32x4 xa = *reinterpret_cast<const f32x4 *>(&kq_s[b3][half ^ 1][li * kKS + col]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                Mp = mfma(ma[r], S[t4][r], Mp);
+                Xp = mfma(xa[r], S[t4][r], Xp);
+            }
+        }
+        x_s[w][l] = Xp;
+        if (c + 2 < nc) stage(c + 2);
+        solve(c);          // wave 0, after its own products
+        __syncthreads();   // partials visible; chunk c + 2 staged; T, G of chunk c visible
+
+        // chunk quantities of head m: T[li][4g..], G[li][4g..] / sqrt(D), beta, P, D at 4g..
+        const f32x4 Tr = *reinterpret_cast<const f32x4 *>(&t_s[par][m][li * kTS + 4 * g]);
+        const f32x4 Gr = *reinterpret_cast<const f32x4 *>(&g_s[par][m][li * kTS + 4 * g]);
+        const f32x4 Br = *reinterpret_cast<const f32x4 *>(&ab_s[b3][1][m][4 * g]);
+        const f32x4 Pr = *reinterpret_cast<const f32x4 *>(&pd_s[b3][0][m][4 * g]);
+        const f32x4 Dr = *reinterpret_cast<const f32x4 *>(&pd_s[b3][1][m][4 * g]);
+        const float p15 = pd_s[b3][0][m][kC - 1];
+        // gam S -> P_15 gam S + K^T (C' diag(D))^T: the decay is kept in gam
+        // while it stays in [2^-60, 2^60] and folded into S otherwise.
+        // 1 / gam' is the hardware reciprocal: the scale of one chunk's
+        // contribution is off by an ulp or so, far inside the tolerance.
+        const float gc = gam;
+        float gnew = gc * p15;
+        float cscale;
+        if (__builtin_expect(gnew >= 0x1p-60f && gnew <= 0x1p60f, 1)) {
+            cscale = __builtin_amdgcn_rcpf(gnew);
+        } else {
+#pragma unroll
+            for (int t4 = 0; t4 < 4; ++t4) S[t4] *= gnew;
+            gnew = 1.0f;
+            cscale = 1.0f;
+        }
+        gam = gnew;
+        const f32x4 Ds = Dr * cscale;
+        // The strip's chain is split between its halves: half 0 forms
+        // R = beta (v - P gam U) and C' = T R and passes C' on through LDS;
+        // half 1 forms O = P gam W + G C' and stores the four tokens.  Both
+        // update their own columns with C'.
+        f32x4 X;
+        __builtin_amdgcn_s_setprio(2);   // the strip's dependent chain ahead of other waves' products
+        if (half == 0) {
+            const f32x4 U = Mp + x_s[w ^ 1][l];
+            f32x4 Rv;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Rv[r] = Br[r] * (vv[r] - Pr[r] * gc * U[r]);
+            X = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) X = mfma(Tr[r], Rv[r], X);
+            c_s[2 * m + strip][l] = X;
+            __builtin_amdgcn_s_setprio(0);
+        } else {
+            const f32x4 W = Mp + x_s[w ^ 1][l];
+            const float gs = gc * a.scale;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) X[r] = Pr[r] * gs * W[r];
+        }
+        __syncthreads();   // C' visible
+        if (half == 1) {
+            const f32x4 Cp = c_s[2 * m + strip][l];
+            f32x4 O = X;   // G carries the 1 / sqrt(D) of the output
+#pragma unroll
+            for (int r = 0; r < 4; ++r) O = mfma(Gr[r], Cp[r], O);
+            const __amdgpu_buffer_rsrc_t ro =
+                buf_rsrc(o0 + (int64_t)t0 * a.out_stride, (int64_t)(T - t0) * a.out_stride * 4);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) buf_store1(ro, o_off + r * o_step, O[r]);
+            X = Cp;
+            __builtin_amdgcn_s_setprio(0);
+        }
+
+        X *= Ds;
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+            for (int t4 = 0; t4 < 4; ++t4) S[t4] = mfma(kcv[4 * s4 + t4], X[s4], S[t4]);
+
+        if (c + 2 < nc) {
+            tiles(c + 2);
+            range_products(c + 2);
+        }
+        // loads for the next chunks go out after this chunk's stores
+        if (c + 3 < nc) prefetch(c + 3);
+        if (c + 1 < nc) load_v(c + 1);
+    }
+
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) *reinterpret_cast<f32x4 *>(srow + 16 * t4) = S[t4] * gam;
+}
+
+bool seq_group_fits(const StepArgs &a) {
+    // at most four value heads per key head (16 waves); the grid and the 32-bit
+    // lane offsets of the buffer loads and stores, which reach the last row of
+    // a whole chunk (padding rows included), must fit
+    const int r = a.nv / a.nk;
+    int64_t widest = a.qk_stride > a.v_stride ? a.qk_stride : a.v_stride;
+    widest = widest > a.out_stride ? widest : a.out_stride;
+    const int64_t rows = a.seq_len > kC ? a.seq_len : kC;
+    return r >= 1 && r <= 4 && (int64_t)a.batch * a.nk * 4 <= INT32_MAX &&
+           ((int64_t)a.batch * a.seq_len * a.nv + 15) / 16 <= INT32_MAX &&
+           rows * widest * 4 + 1024 <= INT32_MAX;
+}
+
+hipError_t launch_seq_group(const StepArgs &a, OutMode mode, hipStream_t stream) {
+    if (mode != kOutRawF32 && mode != kOutNormF32) return hipErrorInvalidValue;
+    const int nc = (a.seq_len + kC - 1) / kC;
+    const unsigned grid = (unsigned)((int64_t)a.batch * a.nk * 4);
+    switch (a.nv / a.nk) {
+        case 1: hipLaunchKernelGGL((seq_group_kernel<1>), dim3(grid), dim3(256), 0, stream, a, nc); break;
+        case 2: hipLaunchKernelGGL((seq_group_kernel<2>), dim3(grid), dim3(512), 0, stream, a, nc); break;
+        case 3: hipLaunchKernelGGL((seq_group_kernel<3>), dim3(grid), dim3(768), 0, stream, a, nc); break;
+        case 4: hipLaunchKernelGGL((seq_group_kernel<4>), dim3(grid), dim3(1024), 0, stream, a, nc); break;
+        default: return hipErrorInvalidValue;
+    }
+    const hipError_t e = hipGetLastError();
+    // with z the output rows get the gated norm in a second pass (four
+    // workgroups hold a head's rows between them)
+    if (e != hipSuccess || mode == kOutRawF32) return e;
+    return launch_norm_rows(a, stream);
+}
+
+}  // namespace gdn

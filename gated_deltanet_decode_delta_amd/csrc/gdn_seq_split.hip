@@ -28,33 +28,13 @@
 // waves on each SIMD of 192 CUs).  Waves of different workgroups share a SIMD,
 // so one workgroup's barrier and chain latency are covered by the others'
 // products.
+#include "gdn_chunk.h"
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
 namespace gdn {
 
-namespace {
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kD = 128;
-constexpr int kC = 16;            // tokens per chunk
-constexpr int kKS = kD + 4;       // LDS row stride (floats) of k / q
-constexpr int kTS = kC + 4;       // LDS row stride of 16x16 matrices in the pre-pass (16-byte rows)
-
-__device__ __forceinline__ f32x4 mfma(float a, float b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-// The value of the lane N places higher in the same 16-lane DPP row, or 1 past
-// the end of the row.
-template <int N>
-__device__ __forceinline__ float dpp_from_above(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(x), 0x100 + N,
-                                                      0xF, 0xF, false));
-}
-
-}  // namespace
+using namespace chunk;
 
 // ---------------------------------------------------------------------------
 // Pre-pass: one wave per (sequence b, key head kh, chunk c).  Tokens past T
@@ -198,27 +178,6 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) pr
             __syncthreads();   // m_s, a_s, t_s free for the next head
         }
     }
-}
-
-// ---------------------------------------------------------------------------
-// Raw buffer descriptors.  A descriptor covers nbytes from p (stride 0); the
-// hardware range check on the lane offset (offset + instruction offset) makes
-// a load at or past nbytes return 0 and drops a store there.  The state pass
-// moves each descriptor's base to the chunk's first row, so that the lane
-// offsets stay fixed over the loop and the rows past T need no predicate.
-// Callers keep every extent below 2^31 bytes.
-__device__ inline __amdgpu_buffer_rsrc_t buf_rsrc(const float *p, int64_t nbytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p), (short)0,
-                                             nbytes > 0 ? (int)nbytes : 0, 0x00020000);
-}
-__device__ inline f32x4 buf_load4(__amdgpu_buffer_rsrc_t r, int off) {
-    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-__device__ inline float buf_load1(__amdgpu_buffer_rsrc_t r, int off) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
-}
-__device__ inline void buf_store1(__amdgpu_buffer_rsrc_t r, int off, float x) {
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), r, off, 0, 0);
 }
 
 // ---------------------------------------------------------------------------

@@ -61,11 +61,12 @@ def test_pmc_record_scaling_and_hash_gate(tmp_path, monkeypatch):
     detail = json.loads((tmp_path / "detail.json").read_text())["kernels"]
     assert detail[kernel]["valu_insts_per_wave"] == pytest.approx(240.0)
     # verify: the first half of its dispatches is T = 2, the second T = 4
-    v = detail[verify]
+    v2, v4 = detail[verify + " [T=2]"], detail[verify + " [T=4]"]
     t2 = 64 * 3 * 48 * 128 * 128 * 4.0 + 64 * 2 * 48 * (bench.head_bytes(128, 48, 16, 4, 4, True)
                                                           - 2 * 128 * 128 * 4)
-    assert v["algorithmic_bytes_per_launch"][0] == int(t2)
-    assert v["algorithmic_bytes_per_launch"][1] > v["algorithmic_bytes_per_launch"][0]
+    assert v2["algorithmic_bytes_per_launch"][0] == int(t2)
+    assert v4["algorithmic_bytes_per_launch"][0] > v2["algorithmic_bytes_per_launch"][0]
+    assert v2["FETCH_SIZE"] == pytest.approx(1000.0) and v4["FETCH_SIZE"] == pytest.approx(3000.0)
     assert "verify_kernel" in (tmp_path / "table.md").read_text()
     # a record taken on other kernel sources is not reported
     rec["kernel_hash"] = "0" * 16
