@@ -26,17 +26,20 @@
 // three waves per SIMD, against 192 workgroups of eight waves for the kernel
 // that gives each head one workgroup.
 //
-// The chunk-level work runs ahead of the state work.  During chunk c (two
-// workgroup barriers):
-//   before the first: U / W products (every wave); chunk c + 2 staged
+// One workgroup barrier per chunk.  The two halves of a strip exchange their
+// partial products over their 64 columns (half 0 hands over its U and W parts,
+// half 1 its U part) and then both form C' = T R, so nothing else has to pass
+// between them within the chunk; the exchange buffers alternate by chunk parity
+// and alpha, beta, P and D are kept four chunks deep, so a wave that runs ahead
+// into the next chunk never overwrites what a slower one still reads.  The
+// chunk-level work runs ahead of the state work.  During chunk c:
+//   before the barrier: U / W products (every wave); chunk c + 2 staged
 //     (k, q, alpha, beta); then A, T and G of chunk c (wave 0, after its own
 //     products);
-//   between them: the strip chains (R, C' in half 0; the first term of O in
-//     half 1) and nothing else, since every wave waits on this short phase
-//     (chunk work placed there on the half-1 waves made the kernel 20% slower);
-//   after the second: O and its stores, the state update; chunk c + 2's k.k /
-//     k.q partial tiles (waves 1..3) and range products M, P, D (one wave per
-//     SIMD); the loads of chunk c + 3's k, q, alpha, beta and chunk c + 1's v.
+//   after it: the strip chains (R, C'; O and its stores in half 1), the state
+//     update; chunk c + 2's k.k / k.q partial tiles (waves 1..3) and range
+//     products M, P, D (one wave per SIMD); the loads of chunk c + 3's k, q,
+//     alpha, beta and chunk c + 1's v.
 #include "gdn_chunk.h"
 #include "gdn_device.h"
 #include "gdn_launch.h"
@@ -54,20 +57,19 @@ constexpr int kBufs = 3;        // k, q, alpha, beta, P, D: chunks c, c + 1, c +
 template <int R>
 __global__ void __launch_bounds__(256 * R) seq_group_kernel(StepArgs a, int nc) {
     constexpr int NT = 256 * R;
-    constexpr int NW = 4 * R;
     constexpr int KQP = (512 + NT - 1) / NT;   // 16-byte pieces of a chunk's k (and of q) per thread
     constexpr int kParts = 3;                   // partial k.k / k.q tiles (waves 1..3)
     __shared__ __align__(16) float kq_s[kBufs][2][kC * kKS];   // [chunk % 3][k, q] rows of a chunk
-    __shared__ __align__(16) float ab_s[kBufs][2][R][kC];      // [chunk % 3][alpha, beta][head]
-    __shared__ __align__(16) float pd_s[kBufs][2][R][kC];      // [chunk % 3][P, D][head]
+    __shared__ __align__(16) float ab_s[4][2][R][kC];          // [chunk % 4][alpha, beta][head]
+    __shared__ __align__(16) float pd_s[4][2][R][kC];          // [chunk % 4][P, D][head]
     __shared__ f32x4 part_s[2][kParts][2][64];                 // [chunk & 1][part][k.k, k.q]
     __shared__ __align__(16) float m_s[2][R][kC * kTS];        // [chunk & 1] M[t][s]
-    __shared__ __align__(16) float mt_s[2][R][kC * kTS];       // [chunk & 1] M^T
     __shared__ __align__(16) float t_s[2][R][kC * kTS];        // [chunk & 1] T row-major
     __shared__ __align__(16) float g_s[2][R][kC * kTS];        // [chunk & 1] G / sqrt(D) row-major
     __shared__ __align__(16) float a_s[R][kC * kTS];           // a_s[s][t] = A[t][s] of the chunk solved
-    __shared__ f32x4 x_s[NW][64];                              // each wave's partial its partner needs
-    __shared__ f32x4 c_s[2 * R][64];                           // C' of each strip
+    // [chunk & 1][strip][U from half 0, W from half 0, U from half 1]: the
+    // partial products over each half's 64 columns that the strip exchanges
+    __shared__ f32x4 x_s[2][2 * R][3][64];
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -154,8 +156,8 @@ __global__ void __launch_bounds__(256 * R) seq_group_kernel(StepArgs a, int nc) 
             }
         }
         if (ab_thread) {
-            ab_s[b3][0][tid >> 4][tid & 15] = pal;
-            ab_s[b3][1][tid >> 4][tid & 15] = pbe;
+            ab_s[c & 3][0][tid >> 4][tid & 15] = pal;
+            ab_s[c & 3][1][tid >> 4][tid & 15] = pbe;
         }
     };
 
@@ -173,11 +175,11 @@ __global__ void __launch_bounds__(256 * R) seq_group_kernel(StepArgs a, int nc) 
     constexpr int kRangeW0 = R > 1 ? 4 : 0;
     auto range_products = [&](int c) {
         if (w >= kRangeW0 && w < kRangeW0 + 4) {
-            const int b3 = c % kBufs, par = c & 1;
+            const int b4 = c & 3, par = c & 1;
             const int t = 4 * (w - kRangeW0) + g, s = li;
 #pragma unroll
             for (int hm = 0; hm < R; ++hm) {
-                float x = ab_s[b3][0][hm][s < t ? s + 1 : 0];   // index kept inside the row
+                float x = ab_s[b4][0][hm][s < t ? s + 1 : 0];   // index kept inside the row
                 x = s < t ? x : 1.0f;
                 x *= dpp_from_above<1>(x);
                 x *= dpp_from_above<2>(x);
@@ -185,9 +187,8 @@ __global__ void __launch_bounds__(256 * R) seq_group_kernel(StepArgs a, int nc) 
                 x *= dpp_from_above<8>(x);
                 const float v = t >= s ? x : 0.0f;
                 m_s[par][hm][t * kTS + s] = v;
-                mt_s[par][hm][s * kTS + t] = v;
-                if (t == kC - 1) pd_s[b3][1][hm][s] = v;
-                if (s == 0) pd_s[b3][0][hm][t] = ab_s[b3][0][hm][0] * v;
+                if (t == kC - 1) pd_s[b4][1][hm][s] = v;
+                if (s == 0) pd_s[b4][0][hm][t] = ab_s[b4][0][hm][0] * v;
             }
         }
     };
@@ -224,7 +225,7 @@ __global__ void __launch_bounds__(256 * R) seq_group_kernel(StepArgs a, int nc) 
     // above li come out exactly 0 and T[li][li] exactly 1).
     auto solve = [&](int c) {
         if (w == 0) {
-            const int b3 = c % kBufs, par = c & 1;
+            const int b4 = c & 3, par = c & 1;
             f32x4 KK = part_s[par][0][0][l], KQ = part_s[par][0][1][l];
 #pragma unroll
             for (int v2 = 1; v2 < kParts; ++v2) {
@@ -234,8 +235,10 @@ __global__ void __launch_bounds__(256 * R) seq_group_kernel(StepArgs a, int nc) 
             const f32x4 KQs = KQ * a.scale;
 #pragma unroll
             for (int hm = 0; hm < R; ++hm) {
-                const f32x4 bet = *reinterpret_cast<const f32x4 *>(&ab_s[b3][1][hm][4 * g]);
-                const f32x4 mA = *reinterpret_cast<const f32x4 *>(&mt_s[par][hm][li * kTS + 4 * g]);  // M[4g+r][li]
+                const f32x4 bet = *reinterpret_cast<const f32x4 *>(&ab_s[b4][1][hm][4 * g]);
+                f32x4 mA;   // M[4g+r][li]
+#pragma unroll
+                for (int r = 0; r < 4; ++r) mA[r] = m_s[par][hm][(4 * g + r) * kTS + li];
                 const f32x4 mG = *reinterpret_cast<const f32x4 *>(&m_s[par][hm][li * kTS + 4 * g]);   // M[li][4g+r]
                 f32x4 acol;
 #pragma unroll
@@ -270,7 +273,7 @@ __global__ void __launch_bounds__(256 * R) seq_group_kernel(StepArgs a, int nc) 
         }
     };
 
-    // v of the lane's row for tokens 4g .. 4g+3 (half 0 only; rows past T read 0)
+    // v of the lane's row for tokens 4g .. 4g+3 (rows past T read 0)
     const int64_t v0 = row_base * a.v_stride + (int64_t)h * kD;
     const int v_off = (int)((4 * g * a.v_stride + row) * 4);
     const int v_step = (int)(a.v_stride * 4);
@@ -280,10 +283,7 @@ __global__ void __launch_bounds__(256 * R) seq_group_kernel(StepArgs a, int nc) 
         const __amdgpu_buffer_rsrc_t rv =
             buf_rsrc(a.v + v0 + (int64_t)t0 * a.v_stride, (int64_t)(T - t0) * a.v_stride * 4);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            vv[r] = 0.0f;
-            if (half == 0) vv[r] = buf_load1(rv, v_off + r * v_step);
-        }
+        for (int r = 0; r < 4; ++r) vv[r] = buf_load1(rv, v_off + r * v_step);
     };
 
     // Prologue: chunks 0 and 1 staged, their range products and tiles formed;
@@ -327,8 +327,7 @@ __global__ void __launch_bounds__(256 * R) seq_group_kernel(StepArgs a, int nc) 
                 for (int t4 = 0; t4 < 4; ++t4) kcv[4 * s4 + t4] = kc[s4 * kKS + 16 * t4];
         }
         // partial U^T = K S^T and W^T = Q S^T over this wave's 64 columns: Mp is
-        // the one the wave goes on with (U in half 0, W in half 1), Xp the one
-        // its partner needs
+        // U in half 0 and W in half 1, Xp the other one
         f32x4 Mp = f32x4{0.f, 0.f, 0.f, 0.f}, Xp = Mp;
 #pragma unroll
         for (int t4 = 0; t4 < 4; ++t4) {
@@ -341,18 +340,28 @@ __global__ void __launch_bounds__(256 * R) seq_group_kernel(StepArgs a, int nc) 
                 Xp = mfma(xa[r], S[t4][r], Xp);
             }
         }
-        x_s[w][l] = Xp;
+        const int si = 2 * m + strip;
+        if (half == 0) {
+            x_s[par][si][0][l] = Mp;
+            x_s[par][si][1][l] = Xp;
+        } else {
+            x_s[par][si][2][l] = Xp;
+        }
         if (c + 2 < nc) stage(c + 2);
         solve(c);          // wave 0, after its own products
-        __syncthreads();   // partials visible; chunk c + 2 staged; T, G of chunk c visible
+        // The one barrier of the chunk: partials visible; chunk c + 2 staged; T
+        // and G of chunk c visible.  Every buffer written before it is read
+        // after it and not written again before the next chunk's barrier
+        // (partials by chunk parity, alpha / beta / P / D four chunks deep).
+        __syncthreads();
 
         // chunk quantities of head m: T[li][4g..], G[li][4g..] / sqrt(D), beta, P, D at 4g..
+        const int b4 = c & 3;
         const f32x4 Tr = *reinterpret_cast<const f32x4 *>(&t_s[par][m][li * kTS + 4 * g]);
-        const f32x4 Gr = *reinterpret_cast<const f32x4 *>(&g_s[par][m][li * kTS + 4 * g]);
-        const f32x4 Br = *reinterpret_cast<const f32x4 *>(&ab_s[b3][1][m][4 * g]);
-        const f32x4 Pr = *reinterpret_cast<const f32x4 *>(&pd_s[b3][0][m][4 * g]);
-        const f32x4 Dr = *reinterpret_cast<const f32x4 *>(&pd_s[b3][1][m][4 * g]);
-        const float p15 = pd_s[b3][0][m][kC - 1];
+        const f32x4 Br = *reinterpret_cast<const f32x4 *>(&ab_s[b4][1][m][4 * g]);
+        const f32x4 Pr = *reinterpret_cast<const f32x4 *>(&pd_s[b4][0][m][4 * g]);
+        const f32x4 Dr = *reinterpret_cast<const f32x4 *>(&pd_s[b4][1][m][4 * g]);
+        const float p15 = pd_s[b4][0][m][kC - 1];
         // gam S -> P_15 gam S + K^T (C' diag(D))^T: the decay is kept in gam
         // while it stays in [2^-60, 2^60] and folded into S otherwise.
         // 1 / gam' is the hardware reciprocal: the scale of one chunk's
@@ -370,41 +379,33 @@ __global__ void __launch_bounds__(256 * R) seq_group_kernel(StepArgs a, int nc) 
         }
         gam = gnew;
         const f32x4 Ds = Dr * cscale;
-        // The strip's chain is split between its halves: half 0 forms
-        // R = beta (v - P gam U) and C' = T R and passes C' on through LDS;
-        // half 1 forms O = P gam W + G C' and stores the four tokens.  Both
-        // update their own columns with C'.
-        f32x4 X;
+        // Both halves of a strip form R = beta (v - P gam U) and C' = T R (so
+        // no second barrier passes C' between them); half 1 also forms
+        // O = P gam W + G C' and stores the four tokens.  Both update their
+        // own columns with C'.
         __builtin_amdgcn_s_setprio(2);   // the strip's dependent chain ahead of other waves' products
-        if (half == 0) {
-            const f32x4 U = Mp + x_s[w ^ 1][l];
-            f32x4 Rv;
+        const f32x4 U = half == 0 ? Mp + x_s[par][si][2][l] : x_s[par][si][0][l] + Xp;
+        f32x4 Rv;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Rv[r] = Br[r] * (vv[r] - Pr[r] * gc * U[r]);
-            X = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int r = 0; r < 4; ++r) Rv[r] = Br[r] * (vv[r] - Pr[r] * gc * U[r]);
+        f32x4 X = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int r = 0; r < 4; ++r) X = mfma(Tr[r], Rv[r], X);
-            c_s[2 * m + strip][l] = X;
-            __builtin_amdgcn_s_setprio(0);
-        } else {
-            const f32x4 W = Mp + x_s[w ^ 1][l];
-            const float gs = gc * a.scale;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) X[r] = Pr[r] * gs * W[r];
-        }
-        __syncthreads();   // C' visible
+        for (int r = 0; r < 4; ++r) X = mfma(Tr[r], Rv[r], X);
         if (half == 1) {
-            const f32x4 Cp = c_s[2 * m + strip][l];
-            f32x4 O = X;   // G carries the 1 / sqrt(D) of the output
+            const f32x4 Gr = *reinterpret_cast<const f32x4 *>(&g_s[par][m][li * kTS + 4 * g]);
+            const f32x4 W = Mp + x_s[par][si][1][l];
+            const float gs = gc * a.scale;
+            f32x4 O;   // G carries the 1 / sqrt(D) of the output
 #pragma unroll
-            for (int r = 0; r < 4; ++r) O = mfma(Gr[r], Cp[r], O);
+            for (int r = 0; r < 4; ++r) O[r] = Pr[r] * gs * W[r];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) O = mfma(Gr[r], X[r], O);
             const __amdgpu_buffer_rsrc_t ro =
                 buf_rsrc(o0 + (int64_t)t0 * a.out_stride, (int64_t)(T - t0) * a.out_stride * 4);
 #pragma unroll
             for (int r = 0; r < 4; ++r) buf_store1(ro, o_off + r * o_step, O[r]);
-            X = Cp;
-            __builtin_amdgcn_s_setprio(0);
         }
+        __builtin_amdgcn_s_setprio(0);
 
         X *= Ds;
 #pragma unroll
