@@ -110,21 +110,41 @@ def _torch():
     return torch
 
 
+_RAW_STREAM = None
+
+
 def _stream(t, stream):
+    """The HIP stream handle: the caller's, else torch's current stream on the
+    tensor's device (the raw-handle query avoids building a Stream object on
+    every call)."""
+    global _RAW_STREAM
     if stream is not None:
         return int(stream)
-    return int(_torch().cuda.current_stream(t.device).cuda_stream)
+    if _RAW_STREAM is None:
+        torch = _torch()
+        _RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None) or (
+            lambda idx: torch.cuda.current_stream(idx).cuda_stream)
+    return int(_RAW_STREAM(t.get_device()))
 
 
 def _rows(t, rows: int, width: int, name: str, dtype=None):
     """(pointer, row stride in elements) of a ``[rows, >= width]`` row array."""
-    torch = _torch()
     if t is None:
         raise ValueError(f"{name} is required")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
+    if t.dim() == 2:   # the common case, with one query of shape and strides
+        n, wd = t.shape
+        s0, s1 = t.stride()
+        if n != rows:
+            raise ValueError(f"{name}: expected {rows} rows, got {n}")
+        if wd < width:
+            raise ValueError(f"{name}: rows of {wd} < {width} elements")
+        if wd > 1 and s1 != 1:
+            raise ValueError(f"{name}: inner dimension must be contiguous")
+        return t.data_ptr(), int(s0 if rows > 1 else max(wd, width)), t
     if t.dim() > 2:
         if t.shape[-1] < 1:
             raise ValueError(f"{name} is empty")
