@@ -152,8 +152,8 @@ gdn_status gdn_decode_norm_q(float *state, int64_t state_seq_stride,
  * gdn_decode_f16state -- the IEEE binary16 state twin of gdn_decode_norm.
  * The state is read as binary16, all arithmetic is fp32, and the updated state
  * is rounded to nearest-even binary16 on store (subnormals kept).
- * state_seq_stride is the slot pitch in HALVES (it depends on how the pool was
- * sized, not on the head dims).  z == NULL selects the raw output o, which then
+ * state_seq_stride is the slot pitch in HALVES, set by the caller's pool layout
+ * (it may exceed NV * Dv * Dk).  z == NULL selects the raw output o, which then
  * must be GDN_F32; otherwise norm_weight is required and out is y as in
  * gdn_decode_norm.  Source: metrale ssm_gdn_a.rs, launcher
  * `gdn_decode_f16_strided_norm`.

@@ -93,3 +93,11 @@ def test_more_than_one_gpu_is_refused_before_any_gpu_work():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and "--gpus 2" in r.stderr
+
+
+def test_code_hash_ignores_comments_only():
+    a = b"// header\nint f(int x) {  /* inline\n comment */\n  return x + 1;  // tail\n}\n"
+    b = b"// a different header\n\nint f(int x) {\n  return x + 1;\n}\n"
+    c = b"int f(int x) {\n  return x + 2;\n}\n"
+    assert bench.code_text(a) == bench.code_text(b)
+    assert bench.code_text(a) != bench.code_text(c)
