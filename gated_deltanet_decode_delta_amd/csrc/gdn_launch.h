@@ -70,7 +70,7 @@ size_t fused_lds_bytes(int dim, int heads_per_key_head);
 hipError_t launch_seq_mfma(const StepArgs &a, OutMode mode, hipStream_t stream);   // dim 128
 // dim 128 without a workspace: one workgroup per (sequence, key head, quarter)
 // forming its chunk quantities itself; seq_group_fits says whether the shape
-// suits it (at most four value heads per key head, 32-bit lane offsets)
+// suits it (at most three value heads per key head, 32-bit lane offsets)
 bool seq_group_fits(const StepArgs &a);
 hipError_t launch_seq_group(const StepArgs &a, OutMode mode, hipStream_t stream);
 // Floats of one workspace record of the split sequence path: one per (sequence,

@@ -13,18 +13,18 @@
 //     S_end = P_15 S0 + C' diag(M[15][.]) K.
 //
 // Mapping.  With the tiled pairing the value heads of key head g are g, g + NK,
-// ..., g + (R - 1) NK (R = NV / NK), and they all read the same k and q.  One
-// workgroup takes (sequence, key head, quarter): rows 32 quarter .. +31 of each
-// of those R heads, four waves per head laid out as in the workspace path's
-// state pass (wave (strip, half) owns 16 rows x 64 key columns, four 16x16
-// accumulator tiles), 4 R waves in all.  The chunk's k and q are staged once for
-// the R heads, and its k.k / k.q tiles are formed once for them, so forming T
-// and G in the workgroup costs 64 extra matrix-core products per chunk per
-// workgroup (on 12 R-independent product streams of 52) and one triangular
-// solve for the R heads side by side (lane group g solves head g).  At the real
-// shape (B = 4, NK = 16, R = 3) that is 256 workgroups of 12 waves, one per CU,
-// three waves per SIMD, against 192 workgroups of eight waves for the kernel
-// that gives each head one workgroup.
+// ..., g + (R - 1) NK (R = NV / NK, at most 3), and they all read the same k
+// and q.  One workgroup takes (sequence, key head, quarter): rows 32 quarter ..
+// +31 of each of those R heads, four waves per head laid out as in the
+// workspace path's state pass (wave (strip, half) owns 16 rows x 64 key
+// columns, four 16x16 accumulator tiles), 4 R waves in all.  The chunk's k
+// and q are staged once for the R heads, and its k.k / k.q tiles are formed
+// once for them, so forming T and G in the workgroup costs 64 extra
+// matrix-core products per chunk per workgroup (on 12 R-independent product
+// streams of 52) and one triangular solve for the R heads side by side (lane
+// group g solves head g).  At the real shape (B = 4, NK = 16, R = 3) that is
+// 256 workgroups of 12 waves, one per CU, three waves per SIMD, against 192
+// workgroups of eight waves for the kernel that gives each head one workgroup.
 //
 // One workgroup barrier per chunk.  The two halves of a strip exchange their
 // partial products over their 64 columns (half 0 hands over its U and W parts,
@@ -51,6 +51,10 @@ using namespace chunk;
 namespace {
 
 constexpr int kBufs = 3;        // k, q, alpha, beta, P, D: chunks c, c + 1, c + 2
+// per-head stride of the 16 x 16 chunk matrices in LDS: four words past a
+// multiple of the bank count, so lane groups that address different heads in
+// one instruction (the solve's stores of T) fall into different banks
+constexpr int kHS = kC * kTS + 4;
 
 }  // namespace
 
@@ -63,10 +67,10 @@ __global__ void __launch_bounds__(256 * R) seq_group_kernel(StepArgs a, int nc) 
     __shared__ __align__(16) float ab_s[4][2][R][kC];          // [chunk % 4][alpha, beta][head]
     __shared__ __align__(16) float pd_s[4][2][R][kC];          // [chunk % 4][P, D][head]
     __shared__ f32x4 part_s[2][kParts][2][64];                 // [chunk & 1][part][k.k, k.q]
-    __shared__ __align__(16) float m_s[2][R][kC * kTS];        // [chunk & 1] M[t][s]
-    __shared__ __align__(16) float t_s[2][R][kC * kTS];        // [chunk & 1] T row-major
-    __shared__ __align__(16) float g_s[2][R][kC * kTS];        // [chunk & 1] G / sqrt(D) row-major
-    __shared__ __align__(16) float a_s[R][kC * kTS];           // a_s[s][t] = A[t][s] of the chunk solved
+    __shared__ __align__(16) float m_s[2][R][kHS];             // [chunk & 1] M[t][s]
+    __shared__ __align__(16) float t_s[2][R][kHS];             // [chunk & 1] T row-major
+    __shared__ __align__(16) float g_s[2][R][kHS];             // [chunk & 1] G / sqrt(D) row-major
+    __shared__ __align__(16) float a_s[R][kHS];                // a_s[s][t] = A[t][s] of the chunk solved
     // [chunk & 1][strip][U from half 0, W from half 0, U from half 1]: the
     // partial products over each half's 64 columns that the strip exchanges
     __shared__ f32x4 x_s[2][2 * R][3][64];
@@ -110,21 +114,25 @@ __global__ void __launch_bounds__(256 * R) seq_group_kernel(StepArgs a, int nc) 
     for (int t4 = 0; t4 < 4; ++t4) S[t4] = *reinterpret_cast<const f32x4 *>(srow + 16 * t4);
     float gam = 1.0f;
 
-    // k and q of a chunk: pieces f = tid + NT u < 512, token f >> 5, columns
-    // (f % 32) * 4, through descriptors based at the chunk's first row (rows past
-    // T read 0); alpha and beta of head e >> 4, token e % 16 for thread e < 16 R
-    // (alpha 1, beta 0 past T: such tokens change nothing).
+    // k and q of a chunk: pieces f = tid + NT u - kqb in [0, 512), token f >> 5,
+    // columns (f % 32) * 4, through descriptors based at the chunk's first row
+    // (rows past T read 0); alpha and beta of head e >> 4, token e % 16 for
+    // e = tid - (NT - 16 R) >= 0 (alpha 1, beta 0 past T: such tokens change
+    // nothing).  The highest threads do it, so that wave 0 goes from its
+    // products to the solve with no staging in between.
+    constexpr int kqb = KQP * NT - 512;
+    const int abe = tid - (NT - 16 * R);
     const int64_t kq0 = row_base * a.qk_stride + (int64_t)kh * kD;
     int kq_off[KQP];
 #pragma unroll
     for (int u = 0; u < KQP; ++u) {
-        const int f = tid + NT * u;
+        const int f = tid + NT * u - kqb;
         kq_off[u] = (int)((((f & 511) >> 5) * a.qk_stride + (f & 31) * 4) * 4);
     }
     f32x4 pk[KQP], pq[KQP];
     float pal = 1.0f, pbe = 0.0f;
-    const bool ab_thread = tid < 16 * R;
-    const int64_t ab_col = kh + (int64_t)(tid >> 4) * a.nk;
+    const bool ab_thread = abe >= 0;
+    const int64_t ab_col = kh + (int64_t)(abe >> 4) * a.nk;
     auto prefetch = [&](int c) {
         const int t0 = c * kC;
         const int64_t off = kq0 + (int64_t)t0 * a.qk_stride;   // uniform
@@ -132,15 +140,15 @@ __global__ void __launch_bounds__(256 * R) seq_group_kernel(StepArgs a, int nc) 
         const __amdgpu_buffer_rsrc_t rk = buf_rsrc(a.k + off, nb), rq = buf_rsrc(a.q + off, nb);
 #pragma unroll
         for (int u = 0; u < KQP; ++u) {
-            if (tid + NT * u < 512) {
+            if (tid + NT * u >= kqb) {
                 pk[u] = buf_load4(rk, kq_off[u]);
                 pq[u] = buf_load4(rq, kq_off[u]);
             }
         }
         pal = 1.0f;
         pbe = 0.0f;
-        if (ab_thread && t0 + (tid & 15) < T) {
-            const int64_t rr = (row_base + t0 + (tid & 15)) * a.ab_stride + ab_col;
+        if (ab_thread && t0 + (abe & 15) < T) {
+            const int64_t rr = (row_base + t0 + (abe & 15)) * a.ab_stride + ab_col;
             pal = a.alpha[rr];
             pbe = a.beta[rr];
         }
@@ -149,15 +157,15 @@ __global__ void __launch_bounds__(256 * R) seq_group_kernel(StepArgs a, int nc) 
         const int b3 = c % kBufs;
 #pragma unroll
         for (int u = 0; u < KQP; ++u) {
-            const int f = tid + NT * u;
-            if (f < 512) {
+            const int f = tid + NT * u - kqb;
+            if (f >= 0) {
                 *reinterpret_cast<f32x4 *>(&kq_s[b3][0][(f >> 5) * kKS + (f & 31) * 4]) = pk[u];
                 *reinterpret_cast<f32x4 *>(&kq_s[b3][1][(f >> 5) * kKS + (f & 31) * 4]) = pq[u];
             }
         }
         if (ab_thread) {
-            ab_s[c & 3][0][tid >> 4][tid & 15] = pal;
-            ab_s[c & 3][1][tid >> 4][tid & 15] = pbe;
+            ab_s[c & 3][0][abe >> 4][abe & 15] = pal;
+            ab_s[c & 3][1][abe >> 4][abe & 15] = pbe;
         }
     };
 
@@ -172,17 +180,21 @@ __global__ void __launch_bounds__(256 * R) seq_group_kernel(StepArgs a, int nc) 
     // lane li the column s.  With x_s = alpha_{s+1} for s < t (else 1), M[t][s]
     // is the suffix product x_s ... x_15 along the 16-lane row (no division, so
     // any alpha >= 0 is exact to fp32 rounding).  Also P_t = alpha_0 M[t][0]
-    // and D[s] = M[15][s].
+    // and D[s] = M[15][s].  Lane s reads alpha_s (one LDS round trip for all
+    // heads) and takes alpha_{s+1} from the lane above.
     constexpr int kRangeW0 = R > 1 ? 4 : 0;
     auto range_products = [&](int c) {
         if (w >= kRangeW0 && w < kRangeW0 + 4) {
             __builtin_amdgcn_s_setprio(2);
             const int b4 = c & 3, par = c & 1;
             const int t = 4 * (w - kRangeW0) + g, s = li;
+            float al[R];
+#pragma unroll
+            for (int hm = 0; hm < R; ++hm) al[hm] = ab_s[b4][0][hm][s];
 #pragma unroll
             for (int hm = 0; hm < R; ++hm) {
-                float x = ab_s[b4][0][hm][s < t ? s + 1 : 0];   // index kept inside the row
-                x = s < t ? x : 1.0f;
+                const float up = dpp_from_above<1>(al[hm]);
+                float x = s < t ? up : 1.0f;
                 x *= dpp_from_above<1>(x);
                 x *= dpp_from_above<2>(x);
                 x *= dpp_from_above<4>(x);
@@ -190,7 +202,7 @@ __global__ void __launch_bounds__(256 * R) seq_group_kernel(StepArgs a, int nc) 
                 const float v = t >= s ? x : 0.0f;
                 m_s[par][hm][t * kTS + s] = v;
                 if (t == kC - 1) pd_s[b4][1][hm][s] = v;
-                if (s == 0) pd_s[b4][0][hm][t] = ab_s[b4][0][hm][0] * v;
+                if (s == 0) pd_s[b4][0][hm][t] = al[hm] * v;
             }
             __builtin_amdgcn_s_setprio(0);
         }
@@ -198,25 +210,35 @@ __global__ void __launch_bounds__(256 * R) seq_group_kernel(StepArgs a, int nc) 
 
     // k.k and k.q tiles in three parts over the 16-column slices: wave 2
     // (SIMD 2) slices 0..3, wave 1 (SIMD 1) slices 4, 5, wave 3 (SIMD 3) slices
-    // 6, 7.  Lane (g, li), register r holds k_{4g+r}.k_{li} and k_{4g+r}.q_{li};
+    // 6, 7, two slices (four 16-byte operand rows, requested together) at a
+    // time.  Lane (g, li), register r holds k_{4g+r}.k_{li} and k_{4g+r}.q_{li};
     // the parts are summed where they are used.
     auto tiles = [&](int c) {
         if (w >= 1 && w <= 3) {
             __builtin_amdgcn_s_setprio(2);
             const int b3 = c % kBufs, par = c & 1;
-            const int part = w - 1, s0 = w == 2 ? 0 : (w == 1 ? 4 : 6), ns = w == 2 ? 4 : 2;
+            const float *kr = &kq_s[b3][0][li * kKS + 4 * g];
+            const float *qr = &kq_s[b3][1][li * kKS + 4 * g];
             f32x4 KK = f32x4{0.f, 0.f, 0.f, 0.f}, KQ = KK;
-            for (int sl = s0; sl < s0 + ns; ++sl) {
-                const f32x4 ka = *reinterpret_cast<const f32x4 *>(&kq_s[b3][0][li * kKS + 16 * sl + 4 * g]);
-                const f32x4 qa = *reinterpret_cast<const f32x4 *>(&kq_s[b3][1][li * kKS + 16 * sl + 4 * g]);
+            auto two_slices = [&](int s0) {
+                f32x4 ka[2], qa[2];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    KK = mfma(ka[r], ka[r], KK);
-                    KQ = mfma(ka[r], qa[r], KQ);
+                for (int i = 0; i < 2; ++i) {
+                    ka[i] = *reinterpret_cast<const f32x4 *>(kr + 16 * (s0 + i));
+                    qa[i] = *reinterpret_cast<const f32x4 *>(qr + 16 * (s0 + i));
                 }
-            }
-            part_s[par][part][0][l] = KK;
-            part_s[par][part][1][l] = KQ;
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        KK = mfma(ka[i][r], ka[i][r], KK);
+                        KQ = mfma(ka[i][r], qa[i][r], KQ);
+                    }
+            };
+            two_slices(w == 2 ? 0 : w == 1 ? 4 : 6);
+            if (w == 2) two_slices(2);
+            part_s[par][w - 1][0][l] = KK;
+            part_s[par][w - 1][1][l] = KQ;
             __builtin_amdgcn_s_setprio(0);
         }
     };
@@ -227,30 +249,41 @@ __global__ void __launch_bounds__(256 * R) seq_group_kernel(StepArgs a, int nc) 
     // symmetric, so no value moves between lanes before LDS.  Then lane group g
     // solves head g: T = (I + A)^{-1} column li by column-oriented forward
     // substitution with the identity column as right-hand side (the entries
-    // above li come out exactly 0 and T[li][li] exactly 1).
+    // above li come out exactly 0 and T[li][li] exactly 1).  Every LDS value
+    // the first part needs is requested at once; the entries of A on and above
+    // the diagonal, which the solve never reads, are masked by a multiply (a
+    // select let the compiler move loads behind a branch and wait on each).
     auto solve = [&](int c) {
         if (w == 0) {
             __builtin_amdgcn_s_setprio(2);
             const int b4 = c & 3, par = c & 1;
-            f32x4 KK = part_s[par][0][0][l], KQ = part_s[par][0][1][l];
+            f32x4 KKp[kParts], KQp[kParts], bet[R], mG[R], mA[R];
 #pragma unroll
-            for (int v2 = 1; v2 < kParts; ++v2) {
-                KK += part_s[par][v2][0][l];
-                KQ += part_s[par][v2][1][l];
+            for (int v2 = 0; v2 < kParts; ++v2) {
+                KKp[v2] = part_s[par][v2][0][l];
+                KQp[v2] = part_s[par][v2][1][l];
             }
-            const f32x4 KQs = KQ * a.scale;
 #pragma unroll
             for (int hm = 0; hm < R; ++hm) {
-                const f32x4 bet = *reinterpret_cast<const f32x4 *>(&ab_s[b4][1][hm][4 * g]);
-                f32x4 mA;   // M[4g+r][li]
+                bet[hm] = *reinterpret_cast<const f32x4 *>(&ab_s[b4][1][hm][4 * g]);
+                mG[hm] = *reinterpret_cast<const f32x4 *>(&m_s[par][hm][li * kTS + 4 * g]);   // M[li][4g+r]
 #pragma unroll
-                for (int r = 0; r < 4; ++r) mA[r] = m_s[par][hm][(4 * g + r) * kTS + li];
-                const f32x4 mG = *reinterpret_cast<const f32x4 *>(&m_s[par][hm][li * kTS + 4 * g]);   // M[li][4g+r]
-                f32x4 acol;
+                for (int r = 0; r < 4; ++r) mA[hm][r] = m_s[par][hm][(4 * g + r) * kTS + li];   // M[4g+r][li]
+            }
+            f32x4 KK = KKp[0], KQ = KQp[0];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acol[r] = li < 4 * g + r ? bet[r] * mA[r] * KK[r] : 0.0f;
-                *reinterpret_cast<f32x4 *>(&a_s[hm][li * kTS + 4 * g]) = acol;
-                *reinterpret_cast<f32x4 *>(&g_s[par][hm][li * kTS + 4 * g]) = mG * KQs;
+            for (int v2 = 1; v2 < kParts; ++v2) {
+                KK += KKp[v2];
+                KQ += KQp[v2];
+            }
+            const f32x4 KQs = KQ * a.scale;
+            f32x4 below;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) below[r] = li < 4 * g + r ? 1.0f : 0.0f;
+#pragma unroll
+            for (int hm = 0; hm < R; ++hm) {
+                *reinterpret_cast<f32x4 *>(&a_s[hm][li * kTS + 4 * g]) = bet[hm] * mA[hm] * KK * below;
+                *reinterpret_cast<f32x4 *>(&g_s[par][hm][li * kTS + 4 * g]) = mG[hm] * KQs;
             }
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
             __builtin_amdgcn_wave_barrier();
@@ -323,16 +356,6 @@ __global__ void __launch_bounds__(256 * R) seq_group_kernel(StepArgs a, int nc) 
     for (int c = 0; c < nc; ++c) {
         const int b3 = c % kBufs, par = c & 1;
         const int t0 = c * kC;
-        // the update's k operands (token 4g + s4, column 64 half + 16 t4 + li),
-        // requested now so that their LDS latency is long past at the update
-        float kcv[16];
-        {
-            const float *kc = &kq_s[b3][0][4 * g * kKS + 64 * half + li];
-#pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4)
-#pragma unroll
-                for (int t4 = 0; t4 < 4; ++t4) kcv[4 * s4 + t4] = kc[s4 * kKS + 16 * t4];
-        }
         // partial U^T = K S^T and W^T = Q S^T over this wave's 64 columns: Mp is
         // U in half 0 and W in half 1, Xp the other one
         f32x4 Mp = f32x4{0.f, 0.f, 0.f, 0.f}, Xp = Mp;
@@ -356,19 +379,38 @@ __global__ void __launch_bounds__(256 * R) seq_group_kernel(StepArgs a, int nc) 
         }
         if (c + 2 < nc) stage(c + 2);
         solve(c);          // wave 0, after its own products
+        // beta, P and D of head m at 4g.. (published by the previous barrier),
+        // read before this one so that their latency is spent waiting at it
+        const int b4 = c & 3;
+        const f32x4 Br = *reinterpret_cast<const f32x4 *>(&ab_s[b4][1][m][4 * g]);
+        const f32x4 Pr = *reinterpret_cast<const f32x4 *>(&pd_s[b4][0][m][4 * g]);
+        const f32x4 Dr = *reinterpret_cast<const f32x4 *>(&pd_s[b4][1][m][4 * g]);
+        const float p15 = pd_s[b4][0][m][kC - 1];
         // The one barrier of the chunk: partials visible; chunk c + 2 staged; T
         // and G of chunk c visible.  Every buffer written before it is read
         // after it and not written again before the next chunk's barrier
         // (partials by chunk parity, alpha / beta / P / D four chunks deep).
         __syncthreads();
 
-        // chunk quantities of head m: T[li][4g..], G[li][4g..] / sqrt(D), beta, P, D at 4g..
-        const int b4 = c & 3;
+        // The strip chain's LDS operands are requested first, in one batch with
+        // no branch on the half (LDS answers a wave's requests in order, so the
+        // chain's first wait covers only them): T[li][4g..] and G[li][4g..] /
+        // sqrt(D) of head m, the other half's U part (slot 2 for half 0, slot 0
+        // for half 1) and half 0's W part (used by half 1).  Then the update's
+        // k operands (token 4g + s4, column 64 half + 16 t4 + li), whose latency
+        // passes under the chain.
         const f32x4 Tr = *reinterpret_cast<const f32x4 *>(&t_s[par][m][li * kTS + 4 * g]);
-        const f32x4 Br = *reinterpret_cast<const f32x4 *>(&ab_s[b4][1][m][4 * g]);
-        const f32x4 Pr = *reinterpret_cast<const f32x4 *>(&pd_s[b4][0][m][4 * g]);
-        const f32x4 Dr = *reinterpret_cast<const f32x4 *>(&pd_s[b4][1][m][4 * g]);
-        const float p15 = pd_s[b4][0][m][kC - 1];
+        const f32x4 Uo = x_s[par][si][2 - 2 * half][l];
+        const f32x4 Gr = *reinterpret_cast<const f32x4 *>(&g_s[par][m][li * kTS + 4 * g]);
+        const f32x4 Wo = x_s[par][si][1][l];
+        float kcv[16];
+        {
+            const float *kc = &kq_s[b3][0][4 * g * kKS + 64 * half + li];
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+                for (int t4 = 0; t4 < 4; ++t4) kcv[4 * s4 + t4] = kc[s4 * kKS + 16 * t4];
+        }
         // gam S -> P_15 gam S + K^T (C' diag(D))^T: the decay is kept in gam
         // while it stays in [2^-60, 2^60] and folded into S otherwise.
         // 1 / gam' is the hardware reciprocal: the scale of one chunk's
@@ -391,7 +433,7 @@ __global__ void __launch_bounds__(256 * R) seq_group_kernel(StepArgs a, int nc) 
         // O = P gam W + G C' and stores the four tokens.  Both update their
         // own columns with C'.
         __builtin_amdgcn_s_setprio(2);   // the strip's dependent chain ahead of other waves' products
-        const f32x4 U = half == 0 ? Mp + x_s[par][si][2][l] : x_s[par][si][0][l] + Xp;
+        const f32x4 U = (half == 0 ? Mp : Xp) + Uo;
         f32x4 Rv;
 #pragma unroll
         for (int r = 0; r < 4; ++r) Rv[r] = Br[r] * (vv[r] - Pr[r] * gc * U[r]);
@@ -399,8 +441,7 @@ __global__ void __launch_bounds__(256 * R) seq_group_kernel(StepArgs a, int nc) 
 #pragma unroll
         for (int r = 0; r < 4; ++r) X = mfma(Tr[r], Rv[r], X);
         if (half == 1) {
-            const f32x4 Gr = *reinterpret_cast<const f32x4 *>(&g_s[par][m][li * kTS + 4 * g]);
-            const f32x4 W = Mp + x_s[par][si][1][l];
+            const f32x4 W = Mp + Wo;
             const float gs = gc * a.scale;
             f32x4 O;   // G carries the 1 / sqrt(D) of the output
 #pragma unroll
@@ -434,14 +475,17 @@ __global__ void __launch_bounds__(256 * R) seq_group_kernel(StepArgs a, int nc) 
 }
 
 bool seq_group_fits(const StepArgs &a) {
-    // at most four value heads per key head (16 waves); the grid and the 32-bit
-    // lane offsets of the buffer loads and stores, which reach the last row of
-    // a whole chunk (padding rows included), must fit
+    // at most three value heads per key head: with four the workgroup has 1024
+    // threads, which caps a wave at 128 VGPRs, and the loop spills (2.15 ms
+    // against 1.22 ms for one workgroup per head at B = 4, T = 4096, NV = 64).
+    // The grid and the 32-bit lane offsets of the buffer loads and stores,
+    // which reach the last row of a whole chunk (padding rows included), must
+    // fit.
     const int r = a.nv / a.nk;
     int64_t widest = a.qk_stride > a.v_stride ? a.qk_stride : a.v_stride;
     widest = widest > a.out_stride ? widest : a.out_stride;
     const int64_t rows = a.seq_len > kC ? a.seq_len : kC;
-    return r >= 1 && r <= 4 && (int64_t)a.batch * a.nk * 4 <= INT32_MAX &&
+    return r >= 1 && r <= 3 && (int64_t)a.batch * a.nk * 4 <= INT32_MAX &&
            ((int64_t)a.batch * a.seq_len * a.nv + 15) / 16 <= INT32_MAX &&
            rows * widest * 4 + 1024 <= INT32_MAX;
 }
@@ -454,7 +498,6 @@ hipError_t launch_seq_group(const StepArgs &a, OutMode mode, hipStream_t stream)
         case 1: hipLaunchKernelGGL((seq_group_kernel<1>), dim3(grid), dim3(256), 0, stream, a, nc); break;
         case 2: hipLaunchKernelGGL((seq_group_kernel<2>), dim3(grid), dim3(512), 0, stream, a, nc); break;
         case 3: hipLaunchKernelGGL((seq_group_kernel<3>), dim3(grid), dim3(768), 0, stream, a, nc); break;
-        case 4: hipLaunchKernelGGL((seq_group_kernel<4>), dim3(grid), dim3(1024), 0, stream, a, nc); break;
         default: return hipErrorInvalidValue;
     }
     const hipError_t e = hipGetLastError();

@@ -1,7 +1,9 @@
 """GPU parity of the workspace-free sequence kernel at D = 128 that gives each
 workgroup one quarter of the state rows of all value heads of a key head.
 
-gdn_recurrence_seq runs it whenever a key head has at most four value heads.
+gdn_recurrence_seq runs it whenever a key head has at most three value heads
+(with four, the one-workgroup-per-head kernel runs: the R = 4 cases below
+check that route).
 Every (value heads per key head, length) pairing below is compared head by head
 with the oracle: ragged lengths (a partial last chunk), lengths under one and
 two chunks, group counts that are and are not multiples of eight (the block
