@@ -31,6 +31,14 @@ __device__ __forceinline__ float dpp_from_above(float x) {
                                                       0xF, 0xF, false));
 }
 
+// The value of the lane N places lower in the same 16-lane DPP row, or 1 before
+// its start (a step of an in-row prefix product).
+template <int N>
+__device__ __forceinline__ float dpp_from_below(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(x), 0x110 + N,
+                                                      0xF, 0xF, false));
+}
+
 // Raw buffer descriptors.  A descriptor covers nbytes from p (stride 0); the
 // hardware range check on the lane offset (offset + instruction offset) makes
 // a load at or past nbytes return 0 and drops a store there.  The kernels move

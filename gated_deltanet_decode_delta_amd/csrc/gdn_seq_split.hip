@@ -41,16 +41,19 @@ using namespace chunk;
 // get alpha 1, beta 0 and zero k, q, so they change nothing.  k and q go
 // straight from global memory into the matrix-core operand layout (lane (g, li)
 // holds row li, columns 16m + 4g .. +3), and the alpha, beta loads of up to 16
-// value heads are issued together, ahead of the work on them.
-// Four waves per SIMD (122 VGPRs, no spill; five or more spill): the pre-pass
-// is bound by its own traffic, so more waves in flight help.
+// value heads are issued together, ahead of the work on them.  Four value
+// heads at a time share the wave: each forms its M, A, G, beta, P and D in
+// turn, then lane group g solves head g, so one substitution serves four heads
+// and only A passes through LDS (M[li][4g..] for G comes from a prefix product
+// along the lane row).  Four waves per SIMD (100 VGPRs, no spill; five spill):
+// the pre-pass is bound by its own traffic, so more waves in flight help.
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) prep_kernel(StepArgs a, float *ws,
                                                                                            int nc) {
     constexpr int kHG = 16;   // value heads whose alpha, beta are staged at once
-    __shared__ __align__(16) float m_s[kC * kTS];   // M[t][s]
-    __shared__ __align__(16) float a_s[kC * kTS];   // a_s[s][t] = A[t][s]
-    __shared__ __align__(16) float t_s[kC * kTS];   // T[t][s]
-    __shared__ float al_s[kHG][kC], be_s[kHG][kC];
+    // per head of four: a_s[s][t] = A[t][s], heads four words apart in the banks
+    __shared__ __align__(16) float a_s[4][kC * kTS + 4];
+    __shared__ __align__(16) float al_s[kHG][kC];
+    __shared__ __align__(16) float be_s[kHG][kC];
 
     const int l = threadIdx.x, g = l >> 4, li = l & 15;
     const int item = blockIdx.x;
@@ -127,55 +130,75 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) pr
         if (m0 + kHG < rep) load_ab(m0 + kHG);
         __syncthreads();
         const int ng = rep - m0 < kHG ? rep - m0 : kHG;
-        for (int mm = 0; mm < ng; ++mm) {
-            const int h = kh + (m0 + mm) * a.nk;   // tiled pairing: value heads kh, kh + NK, ...
-            // M[4g + r][li] by suffix products along the DPP row (no division)
-            f32x4 Mv;
+        // value heads mg .. mg + 3 of the group side by side: lane group g
+        // solves head mg + g
+        for (int mg = 0; mg < ng; mg += 4) {
+            const int nh = ng - mg < 4 ? ng - mg : 4;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 4 * g + r;
-                float x = al_s[mm][li < t ? li + 1 : 0];   // index kept to written entries
-                x = li < t ? x : 1.0f;
-                x *= dpp_from_above<1>(x);
-                x *= dpp_from_above<2>(x);
-                x *= dpp_from_above<4>(x);
-                x *= dpp_from_above<8>(x);
-                Mv[r] = t >= li ? x : 0.0f;
-                m_s[t * kTS + li] = Mv[r];
-                a_s[li * kTS + t] = li < t ? be_s[mm][t] * Mv[r] * KK[r] : 0.0f;
-            }
-            __syncthreads();
-            // T = (I + A)^{-1}, column li per lane: column-oriented forward
-            // substitution, rows of the transposed A read four at a time
-            float x[kC];
+            for (int hm = 0; hm < 4; ++hm) {
+                if (hm >= nh) break;
+                const int mm = mg + hm;
+                const int h = kh + (m0 + mm) * a.nk;   // tiled pairing: value heads kh, kh + NK, ...
+                float *rec = ws + (((int64_t)b * a.nv + h) * nc + c) * kSeqRec;
+                // M[4g + r][li] by suffix products along the DPP row (no division)
+                f32x4 Mv, acol;
 #pragma unroll
-            for (int t = 0; t < kC; ++t) x[t] = t == li ? 1.0f : 0.0f;
-#pragma unroll
-            for (int s2 = 0; s2 < kC - 1; ++s2) {
-#pragma unroll
-                for (int t4 = (s2 + 1) / 4; t4 < kC / 4; ++t4) {
-                    const f32x4 av = *reinterpret_cast<const f32x4 *>(&a_s[s2 * kTS + 4 * t4]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (4 * t4 + e > s2) x[4 * t4 + e] = fmaf(-av[e], x[s2], x[4 * t4 + e]);
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 4 * g + r;
+                    float x = al_s[mm][li < t ? li + 1 : 0];   // index kept to written entries
+                    x = li < t ? x : 1.0f;
+                    x *= dpp_from_above<1>(x);
+                    x *= dpp_from_above<2>(x);
+                    x *= dpp_from_above<4>(x);
+                    x *= dpp_from_above<8>(x);
+                    Mv[r] = t >= li ? x : 0.0f;
+                    acol[r] = li < t ? be_s[mm][t] * Mv[r] * KK[r] : 0.0f;
                 }
-            }
-            if (g == 0) {
-#pragma unroll
-                for (int t = 0; t < kC; ++t) t_s[t * kTS + li] = x[t];
+                *reinterpret_cast<f32x4 *>(&a_s[hm][li * kTS + 4 * g]) = acol;   // a_s[s][t] = A[t][s]
+                // M[li][4g + r] for G: a prefix product along the row gives
+                // alpha_{4g+4} ... alpha_li, and the three below it follow by
+                // one multiply each (1 on the diagonal, 0 above it)
+                float y = li >= 4 * g + 4 ? al_s[mm][li] : 1.0f;
+                y *= dpp_from_below<1>(y);
+                y *= dpp_from_below<2>(y);
+                y *= dpp_from_below<4>(y);
+                y *= dpp_from_below<8>(y);
+                const f32x4 up = *reinterpret_cast<const f32x4 *>(&al_s[mm][4 * g]);   // alpha_{4g} .. alpha_{4g+3}
+                f32x4 Mg;
+                Mg[3] = li >= 4 * g + 3 ? y : 0.0f;
+                Mg[2] = li > 4 * g + 2 ? up[3] * Mg[3] : (li == 4 * g + 2 ? 1.0f : 0.0f);
+                Mg[1] = li > 4 * g + 1 ? up[2] * Mg[2] : (li == 4 * g + 1 ? 1.0f : 0.0f);
+                Mg[0] = li > 4 * g ? up[1] * Mg[1] : (li == 4 * g ? 1.0f : 0.0f);
+                // workspace record: G / sqrt(D) row-major, beta, P, D (T below)
+                *reinterpret_cast<f32x4 *>(rec + 256 + li * kC + 4 * g) = Mg * KQ * a.scale;
+                if (g == 0) rec[512 + li] = be_s[mm][li];
+                if (li == 0) *reinterpret_cast<f32x4 *>(rec + 528 + 4 * g) = al_s[mm][0] * Mv;   // P_t = alpha_0 M[t][0]
+                if (g == 3) rec[544 + li] = Mv[3];                                             // D[s] = M[15][s]
             }
             __syncthreads();
-            // workspace record: T row-major, G / sqrt(D) row-major, beta, P, D
-            float *rec = ws + (((int64_t)b * a.nv + h) * nc + c) * kSeqRec;
-            const f32x4 Tr = *reinterpret_cast<const f32x4 *>(&t_s[li * kTS + 4 * g]);
-            const f32x4 Mr = *reinterpret_cast<const f32x4 *>(&m_s[li * kTS + 4 * g]);
-            *reinterpret_cast<f32x4 *>(rec + li * kC + 4 * g) = Tr;
-            // G[li][4g+r] = M[li][4g+r] k_{4g+r}.q_{li}, times the output's 1 / sqrt(D)
-            *reinterpret_cast<f32x4 *>(rec + 256 + li * kC + 4 * g) = Mr * KQ * a.scale;
-            if (g == 0) rec[512 + li] = be_s[mm][li];
-            if (li == 0) *reinterpret_cast<f32x4 *>(rec + 528 + 4 * g) = al_s[mm][0] * Mv;   // P_t = alpha_0 M[t][0]
-            if (g == 3) rec[544 + li] = Mv[3];                                             // D[s] = M[15][s]
-            __syncthreads();   // m_s, a_s, t_s free for the next head
+            // T = (I + A)^{-1} of head mg + g, column li per lane: column-oriented
+            // forward substitution, rows of the transposed A read four at a
+            // time; the column goes to the record's T (row-major) directly
+            if (g < nh) {
+                float x[kC];
+#pragma unroll
+                for (int t = 0; t < kC; ++t) x[t] = t == li ? 1.0f : 0.0f;
+#pragma unroll
+                for (int s2 = 0; s2 < kC - 1; ++s2) {
+#pragma unroll
+                    for (int t4 = (s2 + 1) / 4; t4 < kC / 4; ++t4) {
+                        const f32x4 av = *reinterpret_cast<const f32x4 *>(&a_s[g][s2 * kTS + 4 * t4]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (4 * t4 + e > s2) x[4 * t4 + e] = fmaf(-av[e], x[s2], x[4 * t4 + e]);
+                    }
+                }
+                const int h = kh + (m0 + mg + g) * a.nk;
+                float *rec = ws + (((int64_t)b * a.nv + h) * nc + c) * kSeqRec;
+#pragma unroll
+                for (int t = 0; t < kC; ++t) rec[t * kC + li] = x[t];
+            }
+            __syncthreads();   // a_s free for the next heads
         }
     }
 }
