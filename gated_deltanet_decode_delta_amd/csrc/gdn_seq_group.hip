@@ -454,6 +454,17 @@ __global__ void __launch_bounds__(256 * R) seq_group_kernel(StepArgs a, int nc) 
             for (int r = 0; r < 4; ++r) buf_store1(ro, o_off + r * o_step, O[r]);
         }
         __builtin_amdgcn_s_setprio(0);
+        // The loads for later chunks go out here, after this chunk's stores and
+        // before the update: chunk c + 3's k, q, alpha, beta, then chunk c + 1's
+        // v (rows past T read 0, so it needs no bound).  The vector memory
+        // counter retires in order, and these are the last memory operations
+        // of the chunk: the staging of chunk c + 3 waits with the four v loads
+        // still in flight, and the next chain's wait for v has nothing younger
+        // to wait for.  Issued after the update, every wave waited on them at
+        // the next chain, most of a memory latency for the late ones (0.936 ->
+        // 0.914 ms).
+        if (c + 3 < nc) prefetch(c + 3);
+        load_v(c + 1);
 
         X *= Ds;
 #pragma unroll
@@ -465,9 +476,6 @@ __global__ void __launch_bounds__(256 * R) seq_group_kernel(StepArgs a, int nc) 
             tiles(c + 2);
             range_products(c + 2);
         }
-        // loads for the next chunks go out after this chunk's stores
-        if (c + 3 < nc) prefetch(c + 3);
-        if (c + 1 < nc) load_v(c + 1);
     }
 
 #pragma unroll
