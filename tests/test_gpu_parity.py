@@ -782,6 +782,27 @@ def test_sequence_workspace_shared_and_odd_heads(g):
     assert np.array_equal(host(st), before)
 
 
+@pytest.mark.parametrize("NK,R", [(2, 2), (1, 4), (1, 5), (2, 8), (1, 17)])
+def test_sequence_many_value_heads_per_key_head(g, seq, NK, R):
+    """Both sequence entries at D = 128 with R = NV / NK value heads per key
+    head: the pre-pass takes them four at a time (R = 5 leaves a group of one,
+    R = 8 makes two full groups) inside groups of sixteen staged alpha / beta
+    rows (R = 17 needs a second one); R >= 4 sends the plain entry to the
+    one-workgroup-per-head kernel.  A ragged T puts a partial chunk last."""
+    B, T, D = 2, 37, 128
+    NV = R * NK
+    c = inputs.make_case(2900 + 10 * R + NK, B=B, NK=NK, NV=NV, D=D, T=T)
+    say("seq heads per key head", NK, R)
+    d = _dev_case(c)
+    st = dev(c.state)
+    o = seq(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"], seq_len=T, num_k_heads=NK,
+            num_v_heads=NV, head_dim=D)
+    ref_st = c.state.copy()
+    ref = orc.seq(ref_st, c.q, c.k, c.v, c.alpha, c.beta, B=B, T=T, NK=NK, NV=NV, Dk=D, Dv=D)
+    assert out_err(host(o), ref, NV, D) < TOL_CHAIN
+    assert tile_err(host(st), ref_st, NV, D) < TOL_CHAIN
+
+
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("T", [1, 15, 16, 17, 32, 33, 48])
 @pytest.mark.parametrize("norm", [False, True])
