@@ -36,10 +36,10 @@
 //   before the barrier: U / W products (every wave); chunk c + 2 staged
 //     (k, q, alpha, beta); then A, T and G of chunk c (wave 0, after its own
 //     products);
-//   after it: the strip chains (R, C'; O and its stores in half 1), the state
+//   after it: the strip chains (R, C'; O and its stores in half 1); the loads
+//     of chunk c + 3's k, q, alpha, beta and chunk c + 1's v; the state
 //     update; chunk c + 2's k.k / k.q partial tiles (waves 1..3) and range
-//     products M, P, D (one wave per SIMD); the loads of chunk c + 3's k, q,
-//     alpha, beta and chunk c + 1's v.
+//     products M, P, D (one wave per SIMD).
 #include "gdn_chunk.h"
 #include "gdn_device.h"
 #include "gdn_launch.h"
@@ -50,7 +50,7 @@ using namespace chunk;
 
 namespace {
 
-constexpr int kBufs = 3;        // k, q, alpha, beta, P, D: chunks c, c + 1, c + 2
+constexpr int kBufs = 3;        // k and q in LDS: chunks c, c + 1, c + 2
 // per-head stride of the 16 x 16 chunk matrices in LDS: four words past a
 // multiple of the bank count, so lane groups that address different heads in
 // one instruction (the solve's stores of T) fall into different banks
