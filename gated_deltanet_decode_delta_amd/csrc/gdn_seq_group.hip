@@ -58,11 +58,17 @@ constexpr int kHS = kC * kTS + 4;
 
 }  // namespace
 
-template <int R>
-__global__ void __launch_bounds__(256 * R) seq_group_kernel(StepArgs a, int nc) {
-    constexpr int NT = 256 * R;
+// SL is the number of row slices a head's 128 rows are split into: 4
+// (quarters, two strips of 16 rows per head, four waves) or, at R = 3 only, 8
+// (eighths, one strip, two waves per head) for grids too small to fill the chip.
+template <int R, int SL>
+__global__ void __launch_bounds__(64 * R * (SL == 4 ? 4 : 2)) seq_group_kernel(StepArgs a, int nc) {
+    static_assert(SL == 4 || (SL == 8 && R == 3), "eighths only at three value heads per key head");
+    constexpr int NSTRIP = SL == 4 ? 2 : 1;    // strips of 16 rows per head in a workgroup
+    constexpr int WPH = 2 * NSTRIP;            // waves per head
+    constexpr int NT = 64 * R * WPH;
     constexpr int KQP = (512 + NT - 1) / NT;   // 16-byte pieces of a chunk's k (and of q) per thread
-    constexpr int kParts = 3;                   // partial k.k / k.q tiles (waves 1..3)
+    constexpr int kParts = SL == 4 ? 3 : 2;     // partial k.k / k.q tiles
     __shared__ __align__(16) float kq_s[kBufs][2][kC * kKS];   // [chunk % 3][k, q] rows of a chunk
     __shared__ __align__(16) float ab_s[4][2][R][kC];          // [chunk % 4][alpha, beta][head]
     __shared__ __align__(16) float pd_s[4][2][R][kC];          // [chunk % 4][P, D][head]
@@ -73,30 +79,30 @@ __global__ void __launch_bounds__(256 * R) seq_group_kernel(StepArgs a, int nc) 
     __shared__ __align__(16) float a_s[R][kHS];                // a_s[s][t] = A[t][s] of the chunk solved
     // [chunk & 1][strip][U from half 0, W from half 0, U from half 1]: the
     // partial products over each half's 64 columns that the strip exchanges
-    __shared__ f32x4 x_s[2][2 * R][3][64];
+    __shared__ f32x4 x_s[2][NSTRIP * R][3][64];
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l = tid & 63, g = l >> 4, li = l & 15;
-    const int m = w >> 2;                    // value head m of the key head
-    const int half = w & 1, strip = (w >> 1) & 1;
+    const int m = w / WPH;                   // value head m of the key head
+    const int half = w & 1, strip = (w >> 1) % NSTRIP;
 
-    // Block -> (sequence, key head, quarter): the four quarters of a key head get
+    // Block -> (sequence, key head, slice): the SL slices of a key head get
     // indices equal modulo 8, so they run on one XCD and share its L2 for the
     // key head's k and q rows.
     const int ngroups = a.batch * a.nk;
     const int full = ngroups / 8 * 8;
-    int grp, quarter;
+    int grp, slice;
     {
         const int bid = blockIdx.x;
-        if (bid < full * 4) {
-            const int r = bid & 31;
-            grp = (bid >> 5) * 8 + (r & 7);
-            quarter = r >> 3;
+        if (bid < full * SL) {
+            const int r = bid % (8 * SL);
+            grp = bid / (8 * SL) * 8 + (r & 7);
+            slice = r >> 3;
         } else {
-            const int r = bid - full * 4, rem = ngroups - full;
+            const int r = bid - full * SL, rem = ngroups - full;
             grp = full + r % rem;
-            quarter = r / rem;
+            slice = r / rem;
         }
     }
     const int b = grp / a.nk;
@@ -104,7 +110,7 @@ __global__ void __launch_bounds__(256 * R) seq_group_kernel(StepArgs a, int nc) 
     const int h = kh + m * a.nk;             // tiled pairing
     const int T = a.seq_len;
     const int64_t row_base = (int64_t)b * T;
-    const int row = 32 * quarter + 16 * strip + li;          // state row (value index) of head h
+    const int row = (kD / SL) * slice + 16 * strip + li;     // state row (value index) of head h
     float *srow = static_cast<float *>(a.state) + (int64_t)b * a.pitch + (int64_t)h * (kD * kD) +
                   (int64_t)row * kD + 64 * half + 4 * g;
 
@@ -181,18 +187,25 @@ __global__ void __launch_bounds__(256 * R) seq_group_kernel(StepArgs a, int nc) 
     // is the suffix product x_s ... x_15 along the 16-lane row (no division, so
     // any alpha >= 0 is exact to fp32 rounding).  Also P_t = alpha_0 M[t][0]
     // and D[s] = M[15][s].  Lane s reads alpha_s (one LDS round trip for all
-    // heads) and takes alpha_{s+1} from the lane above.
+    // heads) and takes alpha_{s+1} from the lane above.  In eighths, waves 1
+    // and 5 (both on SIMD 1) take rows 0..7 and 8..15, two passes each.
     constexpr int kRangeW0 = R > 1 ? 4 : 0;
+    constexpr int kRangePasses = SL == 4 ? 1 : 2;
     auto range_products = [&](int c) {
-        if (w >= kRangeW0 && w < kRangeW0 + 4) {
+        const bool mine = SL == 4 ? (w >= kRangeW0 && w < kRangeW0 + 4) : (w == 1 || w == 5);
+        if (mine) {
             __builtin_amdgcn_s_setprio(2);
             const int b4 = c & 3, par = c & 1;
-            const int t = 4 * (w - kRangeW0) + g, s = li;
+            const int q0 = SL == 4 ? w - kRangeW0 : (w == 1 ? 0 : 2);   // first row quad
+            const int s = li;
             float al[R];
 #pragma unroll
             for (int hm = 0; hm < R; ++hm) al[hm] = ab_s[b4][0][hm][s];
 #pragma unroll
+            for (int pass = 0; pass < kRangePasses; ++pass)
+#pragma unroll
             for (int hm = 0; hm < R; ++hm) {
+                const int t = 4 * (q0 + pass) + g;
                 const float up = dpp_from_above<1>(al[hm]);
                 float x = s < t ? up : 1.0f;
                 x *= dpp_from_above<1>(x);
@@ -208,13 +221,15 @@ __global__ void __launch_bounds__(256 * R) seq_group_kernel(StepArgs a, int nc) 
         }
     };
 
-    // k.k and k.q tiles in three parts over the 16-column slices: wave 2
-    // (SIMD 2) slices 0..3, wave 1 (SIMD 1) slices 4, 5, wave 3 (SIMD 3) slices
-    // 6, 7, two slices (four 16-byte operand rows, requested together) at a
-    // time.  Lane (g, li), register r holds k_{4g+r}.k_{li} and k_{4g+r}.q_{li};
-    // the parts are summed where they are used.
+    // k.k and k.q tiles in parts over the 16-column slices, two slices (four
+    // 16-byte operand rows, requested together) at a time.  In quarters three
+    // parts: wave 2 (SIMD 2) slices 0..3, wave 1 (SIMD 1) slices 4, 5, wave 3
+    // (SIMD 3) slices 6, 7.  In eighths two: wave 2 slices 0..3, wave 3 slices
+    // 4..7 (SIMDs 2 and 3 hold one state wave each there).  Lane (g, li),
+    // register r holds k_{4g+r}.k_{li} and k_{4g+r}.q_{li}; the parts are
+    // summed where they are used.
     auto tiles = [&](int c) {
-        if (w >= 1 && w <= 3) {
+        if (SL == 4 ? (w >= 1 && w <= 3) : (w == 2 || w == 3)) {
             __builtin_amdgcn_s_setprio(2);
             const int b3 = c % kBufs, par = c & 1;
             const float *kr = &kq_s[b3][0][li * kKS + 4 * g];
@@ -235,10 +250,12 @@ __global__ void __launch_bounds__(256 * R) seq_group_kernel(StepArgs a, int nc) 
                         KQ = mfma(ka[i][r], qa[i][r], KQ);
                     }
             };
-            two_slices(w == 2 ? 0 : w == 1 ? 4 : 6);
-            if (w == 2) two_slices(2);
-            part_s[par][w - 1][0][l] = KK;
-            part_s[par][w - 1][1][l] = KQ;
+            const int s0 = SL == 4 ? (w == 2 ? 0 : w == 1 ? 4 : 6) : (w == 2 ? 0 : 4);
+            two_slices(s0);
+            if (SL == 8 || w == 2) two_slices(s0 + 2);
+            const int part = SL == 4 ? w - 1 : w - 2;
+            part_s[par][part][0][l] = KK;
+            part_s[par][part][1][l] = KQ;
             __builtin_amdgcn_s_setprio(0);
         }
     };
@@ -370,7 +387,7 @@ __global__ void __launch_bounds__(256 * R) seq_group_kernel(StepArgs a, int nc) 
                 Xp = mfma(xa[r], S[t4][r], Xp);
             }
         }
-        const int si = 2 * m + strip;
+        const int si = NSTRIP * m + strip;
         if (half == 0) {
             x_s[par][si][0][l] = Mp;
             x_s[par][si][1][l] = Xp;
@@ -501,16 +518,30 @@ bool seq_group_fits(const StepArgs &a) {
 hipError_t launch_seq_group(const StepArgs &a, OutMode mode, hipStream_t stream) {
     if (mode != kOutRawF32 && mode != kOutNormF32) return hipErrorInvalidValue;
     const int nc = (a.seq_len + kC - 1) / kC;
-    const unsigned grid = (unsigned)((int64_t)a.batch * a.nk * 4);
-    switch (a.nv / a.nk) {
-        case 1: hipLaunchKernelGGL((seq_group_kernel<1>), dim3(grid), dim3(256), 0, stream, a, nc); break;
-        case 2: hipLaunchKernelGGL((seq_group_kernel<2>), dim3(grid), dim3(512), 0, stream, a, nc); break;
-        case 3: hipLaunchKernelGGL((seq_group_kernel<3>), dim3(grid), dim3(768), 0, stream, a, nc); break;
+    const int r = a.nv / a.nk;
+    const int64_t ngroups = (int64_t)a.batch * a.nk;
+    // Eighths when a grid of them still runs in one pass over the compute
+    // units (B * NK <= 32 on 256 CUs): twice the workgroups of quarters there.
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 0;
+    const bool eighths = r == 3 && ngroups * 8 <= cus;
+    const unsigned grid = (unsigned)(ngroups * (eighths ? 8 : 4));
+    switch (r) {
+        case 1: hipLaunchKernelGGL((seq_group_kernel<1, 4>), dim3(grid), dim3(256), 0, stream, a, nc); break;
+        case 2: hipLaunchKernelGGL((seq_group_kernel<2, 4>), dim3(grid), dim3(512), 0, stream, a, nc); break;
+        case 3:
+            if (eighths)
+                hipLaunchKernelGGL((seq_group_kernel<3, 8>), dim3(grid), dim3(384), 0, stream, a, nc);
+            else
+                hipLaunchKernelGGL((seq_group_kernel<3, 4>), dim3(grid), dim3(768), 0, stream, a, nc);
+            break;
         default: return hipErrorInvalidValue;
     }
     const hipError_t e = hipGetLastError();
-    // with z the output rows get the gated norm in a second pass (four
-    // workgroups hold a head's rows between them)
+    // with z the output rows get the gated norm in a second pass (four or
+    // eight workgroups hold a head's rows between them)
     if (e != hipSuccess || mode == kOutRawF32) return e;
     return launch_norm_rows(a, stream);
 }

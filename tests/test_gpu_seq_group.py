@@ -3,7 +3,10 @@ workgroup one quarter of the state rows of all value heads of a key head.
 
 gdn_recurrence_seq runs it whenever a key head has at most three value heads
 (with four, the one-workgroup-per-head kernel runs: the R = 4 cases below
-check that route).
+check that route).  At three value heads per key head a grid of eighths (16
+rows per workgroup) runs instead of quarters when it fits the 256 compute
+units in one pass, B * NK <= 32: most small cases below take eighths, and the
+ones marked "quarters" keep B * NK above 32 so that quarters run.
 Every (value heads per key head, length) pairing below is compared head by head
 with the oracle: ragged lengths (a partial last chunk), lengths under one and
 two chunks, group counts that are and are not multiples of eight (the block
@@ -100,3 +103,27 @@ def test_group_kernel_strong_decay_and_zero_alpha(g):
     assert out_err(o, ref, c.NV, 128) < TOL_CHAIN
     assert tile_err(st, ref_st, c.NV, 128) < TOL_CHAIN
     assert np.isfinite(o).all() and np.isfinite(st).all()
+
+
+@pytest.mark.parametrize("B,NK,T,norm", [(3, 12, 17, False), (3, 11, 37, False), (3, 11, 37, True)])
+def test_group_kernel_quarters_at_three_heads(g, B, NK, T, norm):
+    """Quarters at R = 3 (B * NK = 36 or 33, above the eighths limit): a ragged
+    T, group counts with and without a remainder of the mapping's eight."""
+    c = inputs.make_case(3000 + B * NK + T, B=B, NK=NK, NV=3 * NK, D=128, T=T)
+    say("seq group quarters", B, NK, T, norm)
+    o, st, ref, ref_st = _run(g, c, norm)
+    assert out_err(o, ref, c.NV, 128) < TOL_CHAIN
+    assert tile_err(st, ref_st, c.NV, 128) < TOL_CHAIN
+
+
+@pytest.mark.parametrize("B,NK", [(1, 12), (1, 5), (2, 16), (1, 1)])
+def test_group_kernel_eighths_mapping(g, B, NK):
+    """Eighths at R = 3: 12 groups (eight plus a remainder of four), 5 (all in
+    the remainder), 32 (the largest grid that takes eighths: 256 workgroups)
+    and a single group."""
+    T = 40
+    c = inputs.make_case(3100 + B * NK, B=B, NK=NK, NV=3 * NK, D=128, T=T)
+    say("seq group eighths", B, NK)
+    o, st, ref, ref_st = _run(g, c, False)
+    assert out_err(o, ref, c.NV, 128) < TOL_CHAIN
+    assert tile_err(st, ref_st, c.NV, 128) < TOL_CHAIN
