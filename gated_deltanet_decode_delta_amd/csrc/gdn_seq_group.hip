@@ -1,6 +1,7 @@
 // gdn_seq_group.hip -- the T-token recurrence at D = 128 without a workspace:
 // every workgroup forms the chunk quantities it needs itself, for all value
-// heads of one key head, and holds one quarter of their state rows.
+// heads of one key head, and holds one quarter (or, on small grids, one
+// eighth) of their state rows.
 //
 // Same chunked algebra as gdn_seq_mfma.hip and gdn_seq_split.hip (16 tokens per
 // chunk; metrale "layers/ops/ssm_gdn_a.rs" `gdn_prefill_regresident` for the
@@ -25,6 +26,9 @@
 // group g solves head g).  At the real shape (B = 4, NK = 16, R = 3) that is
 // 256 workgroups of 12 waves, one per CU, three waves per SIMD, against 192
 // workgroups of eight waves for the kernel that gives each head one workgroup.
+// Grids of at most 32 key-head groups (B = 1, 2 at NK = 16) would leave CUs
+// idle; at R = 3 they run in eighths: rows 16 eighth .. +15, one strip, two
+// waves per head, twice the workgroups.
 //
 // One workgroup barrier per chunk.  The two halves of a strip exchange their
 // partial products over their 64 columns (half 0 hands over its U and W parts,
