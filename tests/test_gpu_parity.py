@@ -782,6 +782,24 @@ def test_sequence_workspace_shared_and_odd_heads(g):
     assert np.array_equal(host(st), before)
 
 
+@pytest.mark.parametrize("B,NK,R,T", [(3, 11, 3, 37), (1, 16, 3, 40), (2, 16, 3, 17)])
+def test_sequence_workspace_small_batches(g, B, NK, R, T):
+    """The workspace path at 99 value heads in all, and at the real head shape
+    with B = 1 and B = 2 (192 and 384 workgroups, fewer than three per CU),
+    against the oracle on every head, with a ragged or short T."""
+    NV, D = R * NK, 128
+    c = inputs.make_case(3200 + B * NV + T, B=B, NK=NK, NV=NV, D=D, T=T)
+    say("seq workspace row split", B, NK, R, T)
+    d = _dev_case(c)
+    st = dev(c.state)
+    o = g.gdn_recurrence_seq_ws(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"], seq_len=T,
+                                num_k_heads=NK, num_v_heads=NV, head_dim=D)
+    ref_st = c.state.copy()
+    ref = orc.seq(ref_st, c.q, c.k, c.v, c.alpha, c.beta, B=B, T=T, NK=NK, NV=NV, Dk=D, Dv=D)
+    assert out_err(host(o), ref, NV, D) < TOL_CHAIN
+    assert tile_err(host(st), ref_st, NV, D) < TOL_CHAIN
+
+
 @pytest.mark.parametrize("NK,R", [(2, 2), (1, 4), (1, 5), (2, 8), (1, 17)])
 def test_sequence_many_value_heads_per_key_head(g, seq, NK, R):
     """Both sequence entries at D = 128 with R = NV / NK value heads per key
