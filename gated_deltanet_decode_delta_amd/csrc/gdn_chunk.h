@@ -13,8 +13,16 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;
 constexpr int kC = 16;            // tokens per chunk
-constexpr int kKS = kD + 4;       // LDS row stride (floats) of a chunk's k / q rows
-constexpr int kTS = kC + 4;       // LDS row stride of the 16x16 chunk matrices (16-byte rows)
+// LDS row strides (floats).  A 16-byte read by lanes (g, li) of row li,
+// columns 4g .. 4g + 3 is served without bank conflicts on gfx950 when 32
+// lanes fall into distinct 16-byte slots of a 512-byte window, i.e. when the
+// row stride in 16-byte units is 2 mod 4: 24 floats for the 16x16 chunk
+// matrices (20 cost four extra cycles per read).  The k / q rows keep 132:
+// 136 frees their 16-byte reads but puts two-way conflicts on the update's
+// 4-byte reads of a column (token 4g + s, column li), which 132 serves
+// conflict-free, and measured slower.
+constexpr int kKS = kD + 4;       // a chunk's k / q rows
+constexpr int kTS = kC + 8;       // the 16x16 chunk matrices
 
 // One 16x16x4 fp32 matrix-core product: lane l supplies A[l % 16][l / 16] and
 // B[l / 16][l % 16]; the accumulator holds D[4 (l / 16) + r][l % 16] in its

@@ -56,7 +56,7 @@ namespace {
 
 constexpr int kBufs = 3;        // k and q in LDS: chunks c, c + 1, c + 2
 // per-head stride of the 16 x 16 chunk matrices in LDS: four words past a
-// multiple of the bank count, so lane groups that address different heads in
+// multiple of the bank window, so lane groups that address different heads in
 // one instruction (the solve's stores of T) fall into different banks
 constexpr int kHS = kC * kTS + 4;
 
