@@ -62,6 +62,12 @@ def _lib():
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
                            "(hipcc --offload-arch=gfx950)")
+    # torch carries its own HIP runtime under the same soname as ROCm's.  With torch
+    # loaded first, libgdn.so binds to that runtime, so the library and the tensors
+    # and streams it is handed share one runtime.  Loaded the other way round, the
+    # process held two HIP runtimes and every launch of the library failed
+    # (hipErrorNoDevice).
+    _torch()
     lib = ctypes.CDLL(LIB_PATH)
     i64, i32, f32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
     lib.gdn_decode.argtypes = [vp, i64, vp, vp, i64, vp, i64, vp, vp, i64, vp, i64,

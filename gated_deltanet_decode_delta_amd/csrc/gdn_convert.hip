@@ -75,13 +75,11 @@ static unsigned cvt_grid(int64_t n) {
 }
 
 hipError_t launch_f32_to_f16(const float *src, uint16_t *dst, int64_t n, hipStream_t stream) {
-    hipLaunchKernelGGL(f32_to_f16_kernel, dim3(cvt_grid(n)), dim3(kCvtThreads), 0, stream, src, dst, n);
-    return hipGetLastError();
+    return launch(f32_to_f16_kernel, dim3(cvt_grid(n)), dim3(kCvtThreads), 0, stream, src, dst, n);
 }
 
 hipError_t launch_f16_to_f32(const uint16_t *src, float *dst, int64_t n, hipStream_t stream) {
-    hipLaunchKernelGGL(f16_to_f32_kernel, dim3(cvt_grid(n)), dim3(kCvtThreads), 0, stream, src, dst, n);
-    return hipGetLastError();
+    return launch(f16_to_f32_kernel, dim3(cvt_grid(n)), dim3(kCvtThreads), 0, stream, src, dst, n);
 }
 
 }  // namespace gdn

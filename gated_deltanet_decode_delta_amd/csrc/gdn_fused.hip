@@ -419,15 +419,12 @@ template <int D, bool NORM>
 static hipError_t go_fused(const StepArgs &a, const FrontArgs &f, float *ring_out, hipStream_t stream) {
     if (ring_out) {
         const unsigned grid = (unsigned)((int64_t)a.batch * a.nv);
-        hipLaunchKernelGGL((fused_split_kernel<D, NORM>), dim3(grid), dim3(DecodeTile<D, float>::NT), 0,
-                           stream, a, f, ring_out);
-    } else {
-        const unsigned grid = (unsigned)((int64_t)a.batch * a.nk);
-        const size_t lds = fused_lds_bytes(D, a.nv / a.nk);
-        hipLaunchKernelGGL((fused_kernel<D, NORM>), dim3(grid), dim3(DecodeTile<D, float>::NT), lds,
-                           stream, a, f);
+        return launch(fused_split_kernel<D, NORM>, dim3(grid), dim3(DecodeTile<D, float>::NT), 0,
+                      stream, a, f, ring_out);
     }
-    return hipGetLastError();
+    const unsigned grid = (unsigned)((int64_t)a.batch * a.nk);
+    const size_t lds = fused_lds_bytes(D, a.nv / a.nk);
+    return launch(fused_kernel<D, NORM>, dim3(grid), dim3(DecodeTile<D, float>::NT), lds, stream, a, f);
 }
 
 template <bool NORM>

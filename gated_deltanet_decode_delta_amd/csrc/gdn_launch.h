@@ -55,6 +55,21 @@ struct FrontArgs {
 
 constexpr int kMaxTaps = 8;
 
+// Launches `kernel` and returns the status of that launch alone.  A failed HIP
+// call stays recorded in its thread until hipGetLastError reads it, so reading
+// that after a <<<>>> launch would report an earlier failure of the caller's
+// as the library's own.
+template <typename T>
+struct Same {
+    using type = T;
+};
+template <typename... P>
+inline hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                         typename Same<P>::type... args) {
+    void *argv[] = {static_cast<void *>(&args)...};
+    return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, argv, lds, stream);
+}
+
 enum OutMode { kOutRawF32 = 0, kOutNormF32 = 1, kOutNormBF16 = 2, kOutNormQ8 = 3 };
 
 hipError_t launch_decode(const StepArgs &a, int dim, bool f16_state, OutMode mode,

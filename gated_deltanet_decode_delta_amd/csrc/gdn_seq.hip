@@ -333,8 +333,7 @@ static hipError_t go(const StepArgs &a, hipStream_t stream) {
     // Reserving LDS beyond a quarter of the CU's 160 KiB caps residency at three.
     constexpr int kCapBytes = 160 * 1024 / 4 + 1024;
     constexpr int kDyn = seq_static_lds<D, NORM>() < kCapBytes ? kCapBytes - seq_static_lds<D, NORM>() : 0;
-    hipLaunchKernelGGL((seq_kernel<D, NORM>), dim3(grid), dim3(TL::NT), kDyn, stream, a);
-    return hipGetLastError();
+    return launch(seq_kernel<D, NORM>, dim3(grid), dim3(TL::NT), kDyn, stream, a);
 }
 
 template <bool NORM>

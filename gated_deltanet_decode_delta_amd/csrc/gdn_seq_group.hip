@@ -532,18 +532,16 @@ hipError_t launch_seq_group(const StepArgs &a, OutMode mode, hipStream_t stream)
         cus = 0;
     const bool eighths = r == 3 && ngroups * 8 <= cus;
     const unsigned grid = (unsigned)(ngroups * (eighths ? 8 : 4));
+    hipError_t e;
     switch (r) {
-        case 1: hipLaunchKernelGGL((seq_group_kernel<1, 4>), dim3(grid), dim3(256), 0, stream, a, nc); break;
-        case 2: hipLaunchKernelGGL((seq_group_kernel<2, 4>), dim3(grid), dim3(512), 0, stream, a, nc); break;
+        case 1: e = launch(seq_group_kernel<1, 4>, dim3(grid), dim3(256), 0, stream, a, nc); break;
+        case 2: e = launch(seq_group_kernel<2, 4>, dim3(grid), dim3(512), 0, stream, a, nc); break;
         case 3:
-            if (eighths)
-                hipLaunchKernelGGL((seq_group_kernel<3, 8>), dim3(grid), dim3(384), 0, stream, a, nc);
-            else
-                hipLaunchKernelGGL((seq_group_kernel<3, 4>), dim3(grid), dim3(768), 0, stream, a, nc);
+            e = eighths ? launch(seq_group_kernel<3, 8>, dim3(grid), dim3(384), 0, stream, a, nc)
+                        : launch(seq_group_kernel<3, 4>, dim3(grid), dim3(768), 0, stream, a, nc);
             break;
         default: return hipErrorInvalidValue;
     }
-    const hipError_t e = hipGetLastError();
     // with z the output rows get the gated norm in a second pass (four or
     // eight workgroups hold a head's rows between them)
     if (e != hipSuccess || mode == kOutRawF32) return e;

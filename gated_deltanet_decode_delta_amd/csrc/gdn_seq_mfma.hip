@@ -441,8 +441,7 @@ hipError_t launch_seq_mfma(const StepArgs &a, OutMode mode, hipStream_t stream) 
     if (mode != kOutRawF32 && mode != kOutNormF32) return hipErrorInvalidValue;
     // with z the output rows get the gated norm in a second pass: fusing it here
     // (a workgroup-wide sum per token) took 1.56 ms against 1.42 ms for the pair
-    hipLaunchKernelGGL(seq_mfma_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = launch(seq_mfma_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
     if (e != hipSuccess || mode == kOutRawF32) return e;
     return launch_norm_rows(a, stream);
 }

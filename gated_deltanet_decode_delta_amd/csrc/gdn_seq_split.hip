@@ -473,21 +473,17 @@ __global__ void __launch_bounds__(256) norm_rows_kernel(StepArgs a, int64_t item
 hipError_t launch_seq_split(const StepArgs &a, float *ws, hipStream_t stream) {
     const int nc = (a.seq_len + kC - 1) / kC;
     const int64_t items = (int64_t)a.batch * a.nk * nc;
-    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)items), dim3(64), 0, stream, a, ws, nc);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch(prep_kernel, dim3((unsigned)items), dim3(64), 0, stream, a, ws, nc);
     if (e != hipSuccess) return e;
     const unsigned grid = (unsigned)((int64_t)a.batch * a.nv * 4);
-    hipLaunchKernelGGL(split_kernel, dim3(grid), dim3(256), 0, stream, a, (const float *)ws, nc);
-    e = hipGetLastError();
+    e = launch(split_kernel, dim3(grid), dim3(256), 0, stream, a, (const float *)ws, nc);
     if (e != hipSuccess || a.z == nullptr) return e;
     return launch_norm_rows(a, stream);
 }
 
 hipError_t launch_norm_rows(const StepArgs &a, hipStream_t stream) {
     const int64_t rows = (int64_t)a.batch * a.seq_len * a.nv;   // (row, head) pairs
-    hipLaunchKernelGGL(norm_rows_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, a,
-                       rows);
-    return hipGetLastError();
+    return launch(norm_rows_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, a, rows);
 }
 
 }  // namespace gdn

@@ -4,6 +4,7 @@ status codes.  Only calls that validation rejects are made here (they return
 before any HIP call), plus empty calls, which the contract makes no-ops; the
 pointers are fake addresses that are never dereferenced."""
 import ctypes
+import json
 import os
 import re
 import subprocess
@@ -328,3 +329,26 @@ def test_converter_validation(lib):
     assert lib.gdn_state_f32_to_f16(None, p["out"], 64, None) == 1
     assert lib.gdn_state_f16_to_f32(p["state"], p["out"], -1, None) == 2
     assert lib.gdn_state_f16_to_f32(p["state"], p["out"], 0, None) == 0
+
+
+_ONE_RUNTIME = r"""
+import json, sys
+sys.path.insert(0, {root!r})
+import gated_deltanet_decode_delta_amd as gdn
+gdn.lib()                      # the library first, torch only afterwards
+import torch
+maps = open("/proc/self/maps").read().split("\n")
+print(json.dumps(sorted({{ln.split()[-1] for ln in maps if "libamdhip64" in ln}})))
+"""
+
+
+def test_one_hip_runtime_whatever_the_import_order(lib):
+    """torch ships its own HIP runtime under ROCm's soname.  Loading libgdn.so
+    through the binding before torch must still leave a single runtime mapped
+    (regression: the library bound to ROCm's copy, torch then loaded its own,
+    and every launch of the library failed with hipErrorNoDevice)."""
+    res = subprocess.run(["python3", "-c", _ONE_RUNTIME.format(root=ROOT)],
+                         capture_output=True, text=True, timeout=300)
+    assert res.returncode == 0, res.stderr
+    paths = json.loads(res.stdout.strip().splitlines()[-1])
+    assert len(paths) == 1, paths
