@@ -327,6 +327,43 @@ def run_norm_q(g, calls: int, pools: int = 16):
             "hbm_frac_algorithmic": round(algo / ms / 1e6 / HBM_PEAK_GBS, 4)}
 
 
+def run_raw(g, pools: int = 48):
+    """gdn_decode (raw o, no norm) on the B=64 workload, rotated over state
+    pools as the main workload is: median and minimum of 5 trials of 200 calls."""
+    import torch
+    from gated_deltanet_decode_delta_amd import inputs
+
+    c = inputs.config_case("batched")
+    B, NK, NV, D = c.B, c.NK, c.NV, c.D
+    dev = "cuda:0"
+    log(f"[bench] raw decode: B={B} pools={pools}")
+    st0 = torch.from_numpy(c.state).to(dev)
+    states = [st0.clone() for _ in range(pools)]
+    del st0
+    base = {n: torch.from_numpy(getattr(c, n)).to(dev) for n in ("q", "k", "v", "alpha", "beta")}
+    sets = [{n: torch.roll(t, p, dims=0).contiguous() for n, t in base.items()} for p in range(pools)]
+    del base
+    outs = [torch.empty((B, NV * D), dtype=torch.float32, device=dev) for _ in range(pools)]
+
+    def step(i):
+        p = i % pools
+        s = sets[p]
+        g.gdn_decode(states[p], s["q"], s["k"], s["v"], s["alpha"], s["beta"], out=outs[p],
+                     num_k_heads=NK, num_v_heads=NV, head_dim=D)
+
+    trials = sorted(_timed(step, 200, 10) for _ in range(5))
+    ms = trials[2]
+    algo = B * NV * head_bytes(D, NV, NK, 4, 4, False)
+    del states, sets, outs
+    torch.cuda.empty_cache()
+    return {"workload": "raw decode (gdn_decode, no norm), B=64, NV=48, NK=16, D=128, padded "
+                        f"pool, {pools} state pools in rotation",
+            "ms_per_call": round(ms, 5), "min_ms_per_call": round(trials[0], 5),
+            "trials": "median of 5 trials x 200 calls",
+            "state_GBps": round(2.0 * B * NV * D * D * 4 / ms / 1e6, 1),
+            "hbm_frac_algorithmic": round(algo / ms / 1e6 / HBM_PEAK_GBS, 4)}
+
+
 def run_strided(g, calls: int, pools: int = 16):
     """The decode workload on packed projection rows: q | k | v read as column
     slices of one [B, 10240] row (2048 + 2048 + 6144 floats), z at an offset in a
@@ -851,9 +888,9 @@ def main():
     ap.add_argument("--pools", type=int, default=48)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-extra", action="store_true", help="main workload only")
-    ap.add_argument("--extras", default="fp16_state,sequence,verify,norm_q,strided,fused,real_head",
-                    help="comma list of extra workloads: fp16_state, sequence, verify, norm_q, "
-                         "fused, real_head")
+    ap.add_argument("--extras", default="raw,fp16_state,sequence,verify,norm_q,strided,fused,real_head",
+                    help="comma list of extra workloads: raw, fp16_state, sequence, verify, norm_q, "
+                         "strided, fused, real_head")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--seq-only", action="store_true", help="time the sequence workload alone")
     ap.add_argument("--pmc-summarize", metavar="DIR",
@@ -898,7 +935,7 @@ def main():
                          "median_hbm_frac_algorithmic": round(
                              m["algo_bytes"] / m["trials"][2] / 1e6 / HBM_PEAK_GBS, 4)}}
     wanted = [] if args.no_extra else [w for w in args.extras.split(",") if w]
-    runners = {"fp16_state": lambda: run_fp16(g, 100), "sequence": lambda: run_seq(g, 100),
+    runners = {"raw": lambda: run_raw(g), "fp16_state": lambda: run_fp16(g, 100), "sequence": lambda: run_seq(g, 100),
                "verify": lambda: run_verify(g, 100), "norm_q": lambda: run_norm_q(g, 200),
                "strided": lambda: run_strided(g, 200), "fused": lambda: run_fused(g, 200),
                "real_head": lambda: run_real_head(g, 50)}

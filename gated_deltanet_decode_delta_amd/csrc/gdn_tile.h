@@ -23,23 +23,25 @@ struct VecT {
 };
 
 // VPL: state values per lane the workgroup size aims at (the workgroup has
-// D*D/VPL threads, clamped to [64, 1024]); fewer values per lane mean more
-// waves per tile and fewer registers per wave.
-template <int D, typename ST, int VPL = 64>
+// D*ROWS/VPL threads, clamped to [64, 1024]); fewer values per lane mean more
+// waves per tile and fewer registers per wave.  ROWS: rows of the tile one
+// workgroup holds (all D, or a slice of a tile split over workgroups).
+template <int D, typename ST, int VPL = 64, int ROWS = D>
 struct DecodeTile {
     static constexpr int kMaxVec = 16 / (int)sizeof(ST);
     static constexpr int VEC = kMaxVec < D ? kMaxVec : D;     // state elements per vector access
     static constexpr int LPR = (D / VEC) < 16 ? D / VEC : 16; // lanes per row
     static constexpr int NCH = D / (LPR * VEC);               // vectors per lane per row
     static constexpr int C = NCH * VEC;                       // columns per lane
-    static constexpr int NT_RAW = D * D / VPL;
+    static constexpr int NT_RAW = D * ROWS / VPL;
     static constexpr int NT = NT_RAW < 64 ? 64 : (NT_RAW > 1024 ? 1024 : NT_RAW);
     static constexpr int NG = NT / LPR;                       // row groups
-    static constexpr int RPL = (D / NG) < 1 ? 1 : D / NG;     // rows per lane
-    static constexpr int NGA = D / RPL;                       // row groups holding rows
+    static constexpr int RPL = (ROWS / NG) < 1 ? 1 : ROWS / NG;     // rows per lane
+    static constexpr int NGA = ROWS / RPL;                       // row groups holding rows
     static_assert(VEC % 4 == 0, "q/k are read as float4");
     static_assert(RPL <= LPR, "one output row per lane");
     static_assert(NGA <= NG, "rows fit the workgroup");
+    static_assert(D % ROWS == 0, "whole slices");
 };
 
 // Non-temporal store of a state vector (8 or 16 bytes).  The vector goes out as

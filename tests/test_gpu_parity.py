@@ -220,6 +220,20 @@ def test_batched_raw_decode_and_packed_rows(g):
     assert out_err(host(y), ref_y, NV, D) < TOL_STEP
     assert tile_err(host(st), ref_state, NV, D) < TOL_STEP
 
+    # raw o from the packed rows into a window of a wider NaN-filled buffer (the
+    # wide raw launch splits each head's rows over two workgroups)
+    import torch
+    ref_state = c.state.copy()
+    ref_o = orc.decode(ref_state, c.q, c.k, c.v, c.alpha, c.beta, B=B, NK=NK, NV=NV, Dk=D, Dv=D)
+    st = dev(c.state)
+    wide = torch.full((B, NV * D + 36), float("nan"), device="cuda:0")
+    g.gdn_decode(st, pk[:, :qk], pk[:, qk:2 * qk], pk[:, 2 * qk:], abd[:, NV:], abd[:, :NV],
+                 out=wide[:, 4:4 + NV * D], num_k_heads=NK, num_v_heads=NV, head_dim=D)
+    w = host(wide)
+    assert out_err(w[:, 4:4 + NV * D], ref_o, NV, D) < TOL_STEP
+    assert np.isnan(w[:, :4]).all() and np.isnan(w[:, 4 + NV * D:]).all()
+    assert tile_err(host(st), ref_state, NV, D) < TOL_STEP
+
 
 # --------------------------------------------------------------------------- 4
 def test_fp16_state_full_batch(g):
