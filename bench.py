@@ -649,7 +649,7 @@ def calibrate_and_profile(g, steps: int):
     """The program the counter passes run: a plain device copy of a known size
     (to scale FETCH_SIZE / WRITE_SIZE), then `steps` calls of each profiled
     workload, in this order: the B=64 fused-norm decode (8 rotated pools), the
-    B=256 binary16 decode, draft verify at T=2 then T=4 (B=64), the decode with
+    B=64 raw decode (the same pools), the B=256 binary16 decode, draft verify at T=2 then T=4 (B=64), the decode with
     the fused input stage (two ring buffers, B=64) and the B=4, T=4096 sequence
     through both entry points (raw o)."""
     import torch
@@ -675,6 +675,11 @@ def calibrate_and_profile(g, steps: int):
     for i in range(steps):
         g.gdn_decode_norm(st[i % 8], t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["z"], t["gn"],
                           c.eps, out=out, num_k_heads=c.NK, num_v_heads=c.NV)
+    torch.cuda.synchronize()
+    log("[pmc] raw decode B=64")
+    for i in range(steps):
+        g.gdn_decode(st[i % 8], t["q"], t["k"], t["v"], t["alpha"], t["beta"], out=out,
+                     num_k_heads=c.NK, num_v_heads=c.NV, head_dim=c.D)
     torch.cuda.synchronize()
     del st, t, out
 
@@ -747,8 +752,10 @@ def _algorithmic(kernel: str, n_dispatch: int):
     """(label, algorithmic bytes per launch by dispatch index) of the profiled
     decode-shaped kernels, from the figures the bench uses; None otherwise."""
     hb = head_bytes
-    if "decode_kernel<128, float, 1, 16>" in kernel:
+    if "decode_kernel<128, float, 1, 16, 1>" in kernel:
         return "fused-norm decode, B=64", lambda i: 64 * 48 * hb(128, 48, 16, 4, 4, True)
+    if "decode_kernel<128, float, 0, 8, 2>" in kernel:
+        return "raw decode, B=64, two workgroups per head", lambda i: 64 * 48 * hb(128, 48, 16, 4, 4, False)
     if "decode_kernelILi128EDF16_Li2ELi32" in kernel or "decode_kernel<128, _Float16, 2, 32>" in kernel:
         return "binary16 state, bf16 y, B=256", lambda i: 256 * 48 * hb(128, 48, 16, 2, 2, True)
     if "verify_kernel<128, true>" in kernel:
@@ -818,7 +825,7 @@ def pmc_summarize(root: str):
         json.dump(out, f, indent=1)
         f.write("\n")
 
-    main = next(k for k in out["kernels"] if "decode_kernel<128, float, 1, 16>" in k)
+    main = next(k for k in out["kernels"] if "decode_kernel<128, float, 1, 16, 1>" in k)
     m = out["kernels"][main]
     cfg = inputs_batched_algo()
     rec = {
@@ -968,7 +975,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": pmc_traffic(m["algo_bytes"]),
-                     "kernel": "gdn::decode_kernel<128, float, kOutNormF32, 16>",
+                     "kernel": "gdn::decode_kernel<128, float, kOutNormF32, 16, 1>",
                      "algorithmic_bytes_per_launch": int(m["algo_bytes"])},
         "cpu_baseline": cpu,
         "extra": extra,

@@ -29,7 +29,7 @@ def _counter_csv(path, counter, rows):
 
 
 def test_pmc_record_scaling_and_hash_gate(tmp_path, monkeypatch):
-    kernel = "void gdn::decode_kernel<128, float, 1, 16>(gdn::StepArgs)"
+    kernel = "void gdn::decode_kernel<128, float, 1, 16, 1>(gdn::StepArgs)"
     verify = "void gdn::verify_kernel<128, true>(gdn::StepArgs, float*, long)"
     copy = "__amd_rocclr_copyBuffer"
     root = tmp_path / "passes"
@@ -77,7 +77,7 @@ def test_pmc_record_scaling_and_hash_gate(tmp_path, monkeypatch):
 def test_committed_record_names_the_timed_kernel():
     with open(bench.PMC_FILE) as f:
         rec = json.load(f)
-    assert rec["kernel"] == "void gdn::decode_kernel<128, float, 1, 16>(gdn::StepArgs)"
+    assert rec["kernel"] == "void gdn::decode_kernel<128, float, 1, 16, 1>(gdn::StepArgs)"
     assert rec["algorithmic_bytes_per_launch"] == 408_444_928
     assert rec["kernel_sources"] == list(bench.KERNEL_SOURCES)
 
