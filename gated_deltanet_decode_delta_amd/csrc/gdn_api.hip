@@ -423,6 +423,15 @@ gdn_status gdn_recurrence_seq_noalloc(float *state, int64_t state_seq_stride, co
     const int64_t need = gdn_seq_workspace_bytes(batch, seq_len, num_v_heads, k_dim, v_dim);
     if (need < 0) return GDN_ERR_SHAPE;
     if (need > (int64_t)GDN_SEQ_NOALLOC_MAX_BYTES) return GDN_ERR_SCRATCH;
+    // the scratch address is the current device's: a stream of another device
+    // would run the kernels there with this device's address
+    if (stream != nullptr) {
+        int cur = 0;
+        hipDevice_t sdev = 0;
+        if (hipGetDevice(&cur) == hipSuccess && hipStreamGetDevice((hipStream_t)stream, &sdev) == hipSuccess &&
+            sdev != cur)
+            return GDN_ERR_ARG;
+    }
     // every record the state pass reads is written by the pre-pass of the same
     // call first, so nothing in the scratch has to start at zero
     float *ws = nullptr;
@@ -592,7 +601,7 @@ const char *gdn_status_string(gdn_status s) {
         case GDN_ERR_ALIAS: return "GDN_ERR_ALIAS: state/output overlaps another buffer";
         case GDN_ERR_DTYPE: return "GDN_ERR_DTYPE: unsupported output dtype";
         case GDN_ERR_HIP: return "GDN_ERR_HIP: kernel launch failed";
-        case GDN_ERR_ARG: return "GDN_ERR_ARG: invalid scalar argument";
+        case GDN_ERR_ARG: return "GDN_ERR_ARG: invalid scalar argument or stream";
         case GDN_ERR_SCRATCH:
             return "GDN_ERR_SCRATCH: the call needs more than the library's static scratch "
                    "(GDN_SEQ_NOALLOC_MAX_BYTES per GPU)";

@@ -77,7 +77,8 @@ typedef enum gdn_status {
     GDN_ERR_ALIAS = 5,       /* state/out overlaps an input or each other; converter in-place */
     GDN_ERR_DTYPE = 6,       /* out_dtype is not GDN_F32 / GDN_BF16 (or not allowed here)     */
     GDN_ERR_HIP = 7,         /* the kernel launch failed; see gdn_last_hip_error()            */
-    GDN_ERR_ARG = 8,         /* a scalar argument is invalid (eps negative or not finite)     */
+    GDN_ERR_ARG = 8,         /* a scalar argument is invalid (eps negative or not finite), or
+                                a stream of another device (gdn_recurrence_seq_noalloc)        */
     GDN_ERR_SCRATCH = 9      /* gdn_recurrence_seq_noalloc: the shape needs more scratch than
                                 GDN_SEQ_NOALLOC_MAX_BYTES                                      */
 } gdn_status;
@@ -250,14 +251,16 @@ int64_t gdn_seq_workspace_bytes(int32_t batch, int32_t seq_len, int32_t num_v_he
  *   set-up     The library holds one copy of the array per GPU for the life of
  *              the process.  The first call on a device (with that device
  *              current, as for any call: `stream` must belong to the current
- *              device) resolves its address there with hipGetSymbolAddress;
- *              make that first call outside graph capture.
+ *              device, and a stream of another device returns GDN_ERR_ARG)
+ *              resolves its address there with hipGetSymbolAddress; make that
+ *              first call outside graph capture.
  *   sharing    Every call on one GPU uses that GPU's one array, and the array
  *              keeps the last call's contents.  Calls that may overlap on one
  *              GPU (two streams, two host threads) race on it and give wrong
  *              results; order them on one stream.  Nothing in the array needs
  *              to start at zero: each call writes every record it reads.
- * Errors as gdn_recurrence_seq, plus GDN_ERR_SCRATCH.
+ * Errors as gdn_recurrence_seq, plus GDN_ERR_SCRATCH, and GDN_ERR_ARG for a
+ * stream of another device.
  */
 gdn_status gdn_recurrence_seq_noalloc(float *state, int64_t state_seq_stride,
                                       const float *q, const float *k, int64_t qk_stride,

@@ -132,3 +132,20 @@ def test_noalloc_other_head_dim_needs_no_scratch(g):
     ref_o, ref_s = _oracle(c, True)
     assert out_err(host(out), ref_o, c.NV, c.D) < TOL_CHAIN
     assert tile_err(host(st), ref_s, c.NV, c.D) < TOL_CHAIN
+
+
+def test_noalloc_on_a_side_stream(g):
+    """A stream of the current device other than the null stream passes the
+    device check; the results match the workspace entry point on that stream
+    bit for bit, and the oracle."""
+    import torch
+    c = inputs.make_case(2506, B=2, NK=16, NV=48, D=128, T=40)
+    say("noalloc on a side stream")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        oa, sa, ob, sb = _run_pair(g, c, False)
+    assert np.array_equal(oa.view(np.uint32), ob.view(np.uint32))
+    assert np.array_equal(sa.view(np.uint32), sb.view(np.uint32))
+    ref_o, ref_s = _oracle(c, False)
+    assert out_err(oa, ref_o, c.NV, c.D) < TOL_CHAIN
+    assert tile_err(sa, ref_s, c.NV, c.D) < TOL_CHAIN
