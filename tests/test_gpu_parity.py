@@ -348,6 +348,24 @@ def test_sequence_fused_norm_ragged(g, seq):
     assert tile_err(host(st), ref_state, NV, D) < TOL_CHAIN
 
 
+def test_sequence_norm_five_sequences(g, seq):
+    """With z at B=5 (960 state-pass workgroups of the workspace path at NV=48,
+    more than the device holds at once, and 320 quarters in the kernel without
+    a workspace): every head's outputs and state against the oracle."""
+    B, T, NK, NV, D = 5, 40, 16, 48, 128
+    c = inputs.make_case(58, B=B, NK=NK, NV=NV, D=D, T=T)
+    say("sequence norm B=5 T=40")
+    d = _dev_case(c)
+    st = dev(c.state)
+    y = seq(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["z"], d["gn"],
+            c.eps, seq_len=T, num_k_heads=NK, num_v_heads=NV)
+    ref_state = c.state.copy()
+    ref = orc.seq(ref_state, c.q, c.k, c.v, c.alpha, c.beta, B=B, T=T, NK=NK, NV=NV, Dk=D, Dv=D,
+                  z=c.z, gn=c.gn, eps=c.eps)
+    assert out_err(host(y), ref, NV, D) < TOL_CHAIN
+    assert tile_err(host(st), ref_state, NV, D) < TOL_CHAIN
+
+
 def test_sequence_equals_chained_decode(g, seq):
     """T tokens in one sequence launch == T chained single-token launches (1e-4)."""
     B, T, NK, NV, D = 3, 20, 4, 8, 128
@@ -547,6 +565,39 @@ def test_sequence_workspace_deterministic_bitwise(g):
                                     num_v_heads=NV, head_dim=D)
         outs.append((host(st).view(np.uint32), host(o).view(np.uint32)))
     assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+
+
+@pytest.mark.parametrize("T", [70, 200])
+def test_sequence_workspace_norm_two_calls_one_workspace(g, T):
+    """The workspace path with z, twice in one workspace (first filled with NaN)
+    on two different cases of the same shape: nothing the first call leaves in
+    the workspace reaches the second. Each call against the oracle, and the
+    first call's bits again on a fresh workspace."""
+    import torch
+    B, NK, NV, D = 4, 16, 48, 128
+    cases = [inputs.make_case(65 + i, B=B, NK=NK, NV=NV, D=D, T=T) for i in range(2)]
+    say("workspace norm, two calls", T)
+    need = g.gdn_seq_workspace_bytes(B, T, NV, D)
+    ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device="cuda:0")
+
+    def run(c, w):
+        d = _dev_case(c)
+        st = dev(c.state)
+        y = g.gdn_recurrence_seq_ws(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["z"],
+                                    d["gn"], c.eps, workspace=w.view(torch.uint8), seq_len=T,
+                                    num_k_heads=NK, num_v_heads=NV)
+        return host(y), host(st)
+
+    got = [run(c, ws) for c in cases]
+    for c, (y, st) in zip(cases, got):
+        ref_state = c.state.copy()
+        ref = orc.seq(ref_state, c.q, c.k, c.v, c.alpha, c.beta, B=B, T=T, NK=NK, NV=NV, Dk=D,
+                      Dv=D, z=c.z, gn=c.gn, eps=c.eps)
+        assert out_err(y, ref, NV, D) < TOL_CHAIN
+        assert tile_err(st, ref_state, NV, D) < TOL_CHAIN
+    y0, st0 = run(cases[0], torch.zeros_like(ws))
+    assert np.array_equal(y0.view(np.uint32), got[0][0].view(np.uint32))
+    assert np.array_equal(st0.view(np.uint32), got[0][1].view(np.uint32))
 
 
 @pytest.mark.parametrize("kind", ["decode", "f16", "seq128", "seq64", "seq128ws", "seq128ws_norm"])
