@@ -476,6 +476,17 @@ def run_real_head(g, tokens: int):
                               d["gn"], 1e-6, out=d["out"], num_k_heads=NK, num_v_heads=NV)
 
     ms = _timed(token, tokens, 3)
+    # the same 48 calls marshalled once (static buffers, as in a serving loop)
+    calls = [g.prepare(g.gdn_decode_norm, d["state"], d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                       d["z"], d["gn"], 1e-6, out=d["out"], num_k_heads=NK, num_v_heads=NV)
+             for d in layers]
+
+    def token_prepared(i):
+        for call in calls:
+            call()
+
+    ms_prepared = _timed(token_prepared, tokens, 3)
+    del calls
     graph_ms = None
     try:
         s = torch.cuda.Stream()
@@ -494,7 +505,8 @@ def run_real_head(g, tokens: int):
     torch.cuda.empty_cache()
     res = {"workload": "real head B=1, 48 layer states per token, fused norm fp32",
            "us_per_token": round(ms * 1e3, 2), "tokens_per_s": round(1e3 / ms, 1),
-           "state_GBps": round(state_bytes / ms / 1e6, 1)}
+           "state_GBps": round(state_bytes / ms / 1e6, 1),
+           "prepared_us_per_token": round(ms_prepared * 1e3, 2)}
     if graph_ms is not None:
         res.update({"graph_us_per_token": round(graph_ms * 1e3, 2),
                     "graph_state_GBps": round(state_bytes / graph_ms / 1e6, 1)})

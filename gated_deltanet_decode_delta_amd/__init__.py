@@ -5,6 +5,8 @@ functions carry the C names and do argument marshalling only: they read
 pointers, element strides and the current HIP stream off torch tensors and call
 the library, which runs every step of the path in its own gfx950 kernels.  There
 is no fallback: if ``libgdn.so`` is missing or fails to load, every call raises.
+``prepare(entry, ...)`` marshals one call once and returns an object that repeats
+it, so that a loop over static buffers pays for the C call alone.
 
 Tensor conventions (all fp32 CUDA tensors unless noted, inner dim contiguous):
 
@@ -21,6 +23,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import threading
 from typing import Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -181,6 +184,64 @@ def _check(status: int, what: str):
         raise GdnError(status, what)
 
 
+class _Capture(threading.local):
+    active = False
+    record = None
+
+
+_CAPTURE = _Capture()
+
+
+def _invoke(name: str, args: tuple, keep: tuple = ()):
+    """Call the library function ``name`` on marshalled ``args``, or, inside
+    ``prepare``, record the call instead (with tensors made here that the call
+    needs alive)."""
+    if _CAPTURE.active:
+        _CAPTURE.record = (name, args, keep)
+        return
+    _check(getattr(_lib(), name)(*args), name)
+
+
+class PreparedCall:
+    """One entry-point call whose arguments were marshalled once by ``prepare``:
+    calling it launches the same library call again (same tensors, shapes,
+    strides and stream) and returns what the entry point returned."""
+
+    __slots__ = ("_fn", "_args", "_name", "result", "_keep")
+
+    def __init__(self, fn, args, name, result, keep):
+        self._fn, self._args, self._name, self.result, self._keep = fn, args, name, result, keep
+
+    def __call__(self):
+        status = self._fn(*self._args)
+        if status != GDN_OK:
+            raise GdnError(status, self._name)
+        return self.result
+
+
+def prepare(entry, *args, **kwargs) -> PreparedCall:
+    """Marshal one call of an entry point of this module once, for a loop that
+    repeats it on the same buffers (a serving loop's static inputs, outputs and
+    state).  ``entry(*args, **kwargs)`` is checked and marshalled as usual but
+    not launched; the returned object launches it, for the cost of the C call
+    alone.  The stream is the one the call would have used now (``stream=`` or
+    torch's current stream).  The object keeps every tensor the call reads or
+    writes alive; the caller must not resize or free them, and new contents of
+    the same tensors are simply read by the next launch."""
+    if _CAPTURE.active:
+        raise RuntimeError("prepare cannot be nested")
+    _CAPTURE.active, _CAPTURE.record = True, None
+    try:
+        result = entry(*args, **kwargs)
+        record = _CAPTURE.record
+    finally:
+        _CAPTURE.active, _CAPTURE.record = False, None
+    if record is None:
+        raise ValueError(f"{getattr(entry, '__name__', entry)} launches nothing to prepare")
+    name, cargs, keep = record
+    return PreparedCall(getattr(_lib(), name), cargs, name, result, (args, kwargs, keep))
+
+
 def _dims(gn_or_none, num_k_heads, num_v_heads, head_dim):
     if head_dim is None:
         if gn_or_none is None:
@@ -216,8 +277,8 @@ def gdn_decode(state, q, k, v, alpha, beta, out=None, *, num_k_heads: int, num_v
     if abs_ != bs:
         raise ValueError("alpha and beta must share one row stride")
     op, os_, _ = _rows(out, B, NV * D, "out", torch.float32)
-    _check(_lib().gdn_decode(sp, pitch, qp, kp, qs, vp_, vs, ap, bp, abs_, op, os_, B, NK, NV, D,
-                             D, _stream(state, stream)), "gdn_decode")
+    _invoke("gdn_decode", (sp, pitch, qp, kp, qs, vp_, vs, ap, bp, abs_, op, os_, B, NK, NV, D, D,
+                           _stream(state, stream)))
     return out
 
 
@@ -253,9 +314,8 @@ def _norm_call(fn_name, state, state_dtype, q, k, v, alpha, beta, z, norm_weight
     else:
         zp, zs, gp = None, 0, None
     op, os_, _ = _rows(out, B, NV * D, "out", out_dtype)
-    fn = getattr(_lib(), fn_name)
-    _check(fn(sp, pitch, qp, kp, qs, vp_, vs, ap, bp, abs_, zp, zs, gp, float(eps), op, code, os_,
-              B, NK, NV, D, D, _stream(state, stream)), fn_name)
+    _invoke(fn_name, (sp, pitch, qp, kp, qs, vp_, vs, ap, bp, abs_, zp, zs, gp, float(eps), op, code,
+                      os_, B, NK, NV, D, D, _stream(state, stream)))
     return out
 
 
@@ -303,9 +363,9 @@ def gdn_decode_norm_q(state, q, k, v, alpha, beta, z, norm_weight, eps: float = 
         op, os_ = None, 0
     cp, cs, _ = _rows(codes, B, NV * D, "codes", torch.int8)
     scp, scs, _ = _rows(scales, B, NV * D // 32, "scales", torch.float32)
-    _check(_lib().gdn_decode_norm_q(sp, pitch, qp, kp, qs, vp_, vs, ap, bp, abs_, zp, zs,
-                                    norm_weight.data_ptr(), float(eps), op, os_, cp, cs, scp, scs,
-                                    B, NK, NV, D, D, _stream(state, stream)), "gdn_decode_norm_q")
+    _invoke("gdn_decode_norm_q", (sp, pitch, qp, kp, qs, vp_, vs, ap, bp, abs_, zp, zs,
+                                  norm_weight.data_ptr(), float(eps), op, os_, cp, cs, scp, scs,
+                                  B, NK, NV, D, D, _stream(state, stream)))
     return out, codes, scales
 
 
@@ -356,8 +416,7 @@ def gdn_recurrence_seq(state, q, k, v, alpha, beta, z=None, norm_weight=None, ep
     """``seq_len`` tokens per sequence with the state on chip; returns o (or y) rows."""
     out, head, tail = _seq_args(state, q, k, v, alpha, beta, z, norm_weight, out, seq_len,
                                 num_k_heads, num_v_heads, head_dim)
-    _check(_lib().gdn_recurrence_seq(*head, float(eps), *tail, _stream(state, stream)),
-           "gdn_recurrence_seq")
+    _invoke("gdn_recurrence_seq", (*head, float(eps), *tail, _stream(state, stream)))
     return out
 
 
@@ -386,8 +445,8 @@ def gdn_recurrence_seq_ws(state, q, k, v, alpha, beta, z=None, norm_weight=None,
     if not workspace.is_contiguous():
         raise ValueError("workspace must be contiguous")
     nbytes = workspace.numel() * workspace.element_size()
-    _check(_lib().gdn_recurrence_seq_ws(*head, float(eps), *tail, workspace.data_ptr(), nbytes,
-                                        _stream(state, stream)), "gdn_recurrence_seq_ws")
+    _invoke("gdn_recurrence_seq_ws", (*head, float(eps), *tail, workspace.data_ptr(), nbytes,
+                                      _stream(state, stream)), keep=(workspace,))
     return out
 
 
@@ -403,8 +462,7 @@ def gdn_recurrence_seq_noalloc(state, q, k, v, alpha, beta, z=None, norm_weight=
     overlap.  ``out`` is allocated here when not given."""
     out, head, tail = _seq_args(state, q, k, v, alpha, beta, z, norm_weight, out, seq_len,
                                 num_k_heads, num_v_heads, head_dim)
-    _check(_lib().gdn_recurrence_seq_noalloc(*head, float(eps), *tail, _stream(state, stream)),
-           "gdn_recurrence_seq_noalloc")
+    _invoke("gdn_recurrence_seq_noalloc", (*head, float(eps), *tail, _stream(state, stream)))
     return out
 
 
@@ -446,9 +504,9 @@ def gdn_decode_verify(state, q, k, v, alpha, beta, z=None, norm_weight=None, eps
     else:
         zp, zs, gp = None, 0, None
     op, os_, _ = _rows(out, rows, NV * D, "out", torch.float32)
-    _check(_lib().gdn_decode_verify(sp, pitch, ip, ipitch, qp, kp, qs, vp_, vs, ap, bp, abs_, zp, zs,
-                                    gp, float(eps), op, os_, B, T, NK, NV, D, D,
-                                    _stream(state, stream)), "gdn_decode_verify")
+    _invoke("gdn_decode_verify", (sp, pitch, ip, ipitch, qp, kp, qs, vp_, vs, ap, bp, abs_, zp, zs,
+                                  gp, float(eps), op, os_, B, T, NK, NV, D, D,
+                                  _stream(state, stream)))
     return out, inter_state
 
 
@@ -499,10 +557,10 @@ def gdn_decode_fused(state, conv_state, x, conv_weight, br, ar, dt_bias, decay_r
     else:
         zp, zs, gp = None, 0, None
     op, os_, _ = _rows(out, B, NV * D, "out", torch.float32)
-    _check(_lib().gdn_decode_fused(sp, pitch, rp, rpitch, rop, xp, xs, conv_weight.data_ptr(), taps, bp,
-                                   ap, bs, dt_bias.data_ptr(), decay_rate.data_ptr(), float(l2_eps),
-                                   zp, zs, gp, float(eps), op, os_, B, NK, NV, D, D,
-                                   _stream(state, stream)), "gdn_decode_fused")
+    _invoke("gdn_decode_fused", (sp, pitch, rp, rpitch, rop, xp, xs, conv_weight.data_ptr(), taps, bp,
+                                 ap, bs, dt_bias.data_ptr(), decay_rate.data_ptr(), float(l2_eps),
+                                 zp, zs, gp, float(eps), op, os_, B, NK, NV, D, D,
+                                 _stream(state, stream)))
     return out
 
 
@@ -515,8 +573,7 @@ def gdn_state_f32_to_f16(src, dst=None, stream=None):
         dst = torch.empty(src.shape, dtype=torch.float16, device=src.device)
     if dst.dtype != torch.float16 or not dst.is_contiguous() or dst.numel() != src.numel():
         raise ValueError("dst must be a contiguous float16 tensor of the same size")
-    _check(_lib().gdn_state_f32_to_f16(src.data_ptr(), dst.data_ptr(), src.numel(),
-                                       _stream(src, stream)), "gdn_state_f32_to_f16")
+    _invoke("gdn_state_f32_to_f16", (src.data_ptr(), dst.data_ptr(), src.numel(), _stream(src, stream)))
     return dst
 
 
@@ -529,6 +586,5 @@ def gdn_state_f16_to_f32(src, dst=None, stream=None):
         dst = torch.empty(src.shape, dtype=torch.float32, device=src.device)
     if dst.dtype != torch.float32 or not dst.is_contiguous() or dst.numel() != src.numel():
         raise ValueError("dst must be a contiguous fp32 tensor of the same size")
-    _check(_lib().gdn_state_f16_to_f32(src.data_ptr(), dst.data_ptr(), src.numel(),
-                                       _stream(src, stream)), "gdn_state_f16_to_f32")
+    _invoke("gdn_state_f16_to_f32", (src.data_ptr(), dst.data_ptr(), src.numel(), _stream(src, stream)))
     return dst
