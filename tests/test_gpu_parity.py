@@ -445,6 +445,33 @@ def test_every_head_dim_all_entry_points(g, D, NV, NK):
 
 
 # ------------------------------------------------------------- special cases
+@pytest.mark.parametrize("B,NK,NV", [(5, 16, 64), (33, 8, 8), (3, 1, 128), (64, 16, 48)])
+def test_raw_decode_heads_split_over_two_workgroups(g, B, NK, NV):
+    """The wide raw decode at D = 128 splits each head's rows over two
+    workgroups: other pairings (four, one and 128 value heads per key head), a
+    NaN-padded slot pitch and the output in a window of a wider NaN-filled
+    buffer. Every head's output and state tile against the oracle; the pads
+    stay NaN."""
+    import torch
+    D = 128
+    pitch = NV * D * D + 64
+    c = inputs.make_case(2400 + B + NV, B=B, NK=NK, NV=NV, D=D, pitch=pitch)
+    say("raw split", B, NK, NV)
+    d = _dev_case(c)
+    st = dev(c.state)
+    wide = torch.full((B, NV * D + 20), float("nan"), device="cuda:0")
+    g.gdn_decode(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"], out=wide[:, 12:12 + NV * D],
+                 num_k_heads=NK, num_v_heads=NV, head_dim=D)
+    ref_st = c.state.copy()
+    ref = orc.decode(ref_st, c.q, c.k, c.v, c.alpha, c.beta, B=B, NK=NK, NV=NV, Dk=D, Dv=D)
+    w = host(wide)
+    assert out_err(w[:, 12:12 + NV * D], ref, NV, D) < TOL_STEP
+    assert np.isnan(w[:, :12]).all() and np.isnan(w[:, 12 + NV * D:]).all()
+    got = host(st)
+    assert tile_err(got, ref_st, NV, D) < TOL_STEP
+    assert np.isnan(got[:, NV * D * D:]).all()
+
+
 @pytest.mark.parametrize("D", [4, 8, 16, 32, 64, 128, 256])
 def test_wide_launch_every_head_dim(g, D):
     """Launches of 256 or more workgroups use the wide single-token tile (16
