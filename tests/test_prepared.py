@@ -82,3 +82,94 @@ def test_prepared_calls_match_direct_calls():
                                         seq_len=40, num_k_heads=16, num_v_heads=48, head_dim=128)
     assert np.array_equal(host(o_a).view(np.uint32), host(o_b).view(np.uint32))
     assert np.array_equal(host(st_a).view(np.uint32), host(st_b).view(np.uint32))
+
+
+def _bits(t):
+    from gpu_util import host
+    return host(t).view(np.uint16 if t.dtype in (_torch().float16, _torch().bfloat16) else
+                        (np.uint8 if t.dtype == _torch().int8 else np.uint32))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("entry", ["gdn_decode", "gdn_decode_norm_bf16", "gdn_decode_norm_q",
+                                   "gdn_decode_f16state", "gdn_recurrence_seq",
+                                   "gdn_recurrence_seq_noalloc", "gdn_decode_verify",
+                                   "gdn_decode_fused", "gdn_state_f32_to_f16"])
+def test_prepared_call_of_every_entry_point(entry):
+    """Each entry point twice through a prepared call and twice directly, on
+    copies of the same inputs and state: the same bits in every output and in
+    the state."""
+    torch = _torch()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from gated_deltanet_decode_delta_amd import inputs
+    from gpu_util import dev
+    print("[case] prepared", entry, file=sys.stderr, flush=True)
+    B, NK, NV, D = 3, 2, 6, 128
+    T = 5 if entry in ("gdn_recurrence_seq", "gdn_recurrence_seq_noalloc", "gdn_decode_verify") else 1
+    if entry == "gdn_decode_fused":
+        c = inputs.make_frontend_case(2310, B=B, NK=NK, NV=NV, D=D)
+        names = ("x", "w", "br", "ar", "dt", "rate", "z", "gn")
+    else:
+        c = inputs.make_case(2311, B=B, NK=NK, NV=NV, D=D, T=T)
+        names = ("q", "k", "v", "z", "alpha", "beta", "gn")
+    d = {n: dev(getattr(c, n)) for n in names}
+
+    def run(state, ring=None):
+        """The entry point's call on this state (and ring), as (fn, args, kwargs)."""
+        if entry == "gdn_decode":
+            return gdn.gdn_decode, (state, d["q"], d["k"], d["v"], d["alpha"], d["beta"]), \
+                dict(num_k_heads=NK, num_v_heads=NV, head_dim=D)
+        if entry == "gdn_decode_norm_bf16":
+            return gdn.gdn_decode_norm, (state, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["z"],
+                                         d["gn"], c.eps), \
+                dict(out_dtype=torch.bfloat16, num_k_heads=NK, num_v_heads=NV)
+        if entry == "gdn_decode_norm_q":
+            return gdn.gdn_decode_norm_q, (state, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["z"],
+                                           d["gn"], c.eps), dict(num_k_heads=NK, num_v_heads=NV)
+        if entry == "gdn_decode_f16state":
+            return gdn.gdn_decode_f16state, (state, d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                                             d["z"], d["gn"], c.eps), \
+                dict(out_dtype=torch.bfloat16, num_k_heads=NK, num_v_heads=NV)
+        if entry in ("gdn_recurrence_seq", "gdn_recurrence_seq_noalloc"):
+            return getattr(gdn, entry), (state, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["z"],
+                                         d["gn"], c.eps), \
+                dict(seq_len=T, num_k_heads=NK, num_v_heads=NV)
+        if entry == "gdn_decode_verify":
+            return gdn.gdn_decode_verify, (state, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["z"],
+                                           d["gn"], c.eps), \
+                dict(num_tokens=T, num_k_heads=NK, num_v_heads=NV)
+        if entry == "gdn_decode_fused":
+            return gdn.gdn_decode_fused, (state, ring, d["x"], d["w"], d["br"], d["ar"], d["dt"],
+                                          d["rate"], d["z"], d["gn"], 1e-6, 1e-6), \
+                dict(num_k_heads=NK, num_v_heads=NV)
+        return gdn.gdn_state_f32_to_f16, (state,), {}
+
+    def fresh():
+        st = dev(c.state)
+        if entry == "gdn_decode_f16state":
+            st = gdn.gdn_state_f32_to_f16(st)
+        ring = dev(c.ring) if entry == "gdn_decode_fused" else None
+        return st, ring
+
+    def flat(res):
+        return [r for r in (res if isinstance(res, tuple) else (res,)) if r is not None]
+
+    st_a, ring_a = fresh()
+    fn, args, kw = run(st_a, ring_a)
+    call = gdn.prepare(fn, *args, **kw)
+    st_b, ring_b = fresh()
+    for _ in range(2):
+        got_a = flat(call())
+        fn, args, kw = run(st_b, ring_b)
+        got_b = flat(fn(*args, **kw))
+    pairs = list(zip(got_a, got_b)) + [(st_a, st_b)]
+    if ring_a is not None:
+        pairs.append((ring_a, ring_b))
+    for x, y in pairs:
+        assert np.array_equal(_bits(x), _bits(y))
