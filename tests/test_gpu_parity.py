@@ -522,11 +522,14 @@ def test_wide_launch_every_head_dim(g, D):
     assert tile_err(got16, ref16.view(np.float16).astype(np.float64), NV, D) < TOL_F16
 
 
-def test_pins_hold_on_gpu(g):
+@pytest.mark.parametrize("B", [2, 32])
+def test_pins_hold_on_gpu(g, B):
     """The closed-form cases of the oracle pins, on the GPU kernels:
     alpha=1/beta=0 leaves the state bit-identical; alpha=0/beta=1 writes v k^T;
-    one-hot keys with alpha=beta=1 store v in column h mod NK."""
-    B, NK, NV, D = 2, 4, 8, 128
+    one-hot keys with alpha=beta=1 store v in column h mod NK. B = 2 runs the
+    small-grid launch, B = 32 the wide one (each head's rows over two
+    workgroups)."""
+    NK, NV, D = 4, 8, 128
     c = inputs.make_case(61, B=B, NK=NK, NV=NV, D=D)
     say("gpu pins")
     ones = np.ones((B, NV), np.float32)
