@@ -149,3 +149,39 @@ def test_noalloc_on_a_side_stream(g):
     ref_o, ref_s = _oracle(c, False)
     assert out_err(oa, ref_o, c.NV, c.D) < TOL_CHAIN
     assert tile_err(sa, ref_s, c.NV, c.D) < TOL_CHAIN
+
+
+def test_noalloc_captured_in_a_graph(g):
+    """The entry point for callers that cannot allocate, captured once in a HIP
+    graph after a first eager call (which resolves the scratch address), then
+    replayed three times with eager work and synchronisation in between: every
+    replay's output and state equal the same calls made eagerly, bit for bit."""
+    import torch
+    c = inputs.make_case(2507, B=1, NK=16, NV=48, D=128, T=40)
+    say("noalloc in a graph")
+    d = {n: dev(getattr(c, n)) for n in ("q", "k", "v", "z", "alpha", "beta", "gn")}
+    rows, vw = c.B * c.T, c.NV * c.D
+    st_g, st_e = dev(c.state), dev(c.state)
+    out_g = torch.empty((rows, vw), device="cuda:0")
+    out_e = torch.empty((rows, vw), device="cuda:0")
+
+    def call(st, out):
+        assert _call(g, "noalloc", c, st, d, out, False) == 0
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(st_g, out_g)                      # first call outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(st_g, out_g)
+    call(st_e, out_e)                          # the eager copy catches up with the warm-up
+    for rep in range(3):
+        graph.replay()
+        call(st_e, out_e)
+        scratch = torch.randn(1 << 20, device="cuda:0").sum()
+        torch.cuda.synchronize()
+        assert bool(torch.isfinite(scratch))
+        assert torch.equal(out_g, out_e), rep
+        assert torch.equal(st_g, st_e), rep
