@@ -44,6 +44,32 @@ struct DecodeTile {
     static_assert(D % ROWS == 0, "whole slices");
 };
 
+// The state tile's 16-byte accesses go through a buffer descriptor over the
+// head's slot, which carries an explicit cache policy (the CPol bits of a
+// gfx950 buffer instruction: sc0 = 1, nt = 2, sc1 = 16).  The tile is read
+// once and written once per call: the loads stream (nt), and the stores
+// stream and write through at device scope (sc0 sc1 nt).  Against nt stores
+// that took the B=64 fp32 decode from 67.8 to 67.1 us and the B=256 binary16
+// decode from 123.8 to 122.1 us; loads with the same bits, or buffer
+// instructions with nt alone, changed nothing.
+constexpr int kTileLoadPolicy = 2;
+constexpr int kTileStorePolicy = 19;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void *slot, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(slot), (short)0, bytes, 0x00020000);
+}
+template <typename V>
+__device__ __forceinline__ V load_tile_vec(__amdgpu_buffer_rsrc_t r, int byte_off) {
+    static_assert(sizeof(V) == 16, "16-byte vectors");
+    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kTileLoadPolicy));
+}
+template <typename V>
+__device__ __forceinline__ void store_tile_vec(__amdgpu_buffer_rsrc_t r, int byte_off, const V &x) {
+    static_assert(sizeof(V) == 16, "16-byte vectors");
+    typedef unsigned U __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(U, x), r, byte_off, 0, kTileStorePolicy);
+}
+
 // Non-temporal store of a state vector (8 or 16 bytes).  The vector goes out as
 // 32-bit words: hipcc drops the non-temporal hint of the decode's store of a
 // vector of binary16 values (it emits a plain store), but keeps it on words.
