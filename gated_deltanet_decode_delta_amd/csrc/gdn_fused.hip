@@ -58,15 +58,17 @@ fused_kernel(StepArgs a, FrontArgs f) {
     const bool active = grp < TL::NGA;
     const int row0 = grp * RPL;
     float s[RPL][C];
+    // the tiles' vectors through buffer descriptors with the decode's cache policy
+    auto tile_off = [&](int r, int c) { return ((row0 + r) * D + (c * LPR + p) * VEC) * (int)sizeof(float); };
     auto load_tile = [&](int m) {
         const float *slot = static_cast<const float *>(a.state) + (int64_t)b * a.pitch +
                             (int64_t)(g + m * a.nk) * (D * D);
+        const __amdgpu_buffer_rsrc_t srs = tile_rsrc(slot, D * D * (int)sizeof(float));
 #pragma unroll
         for (int r = 0; r < RPL; ++r)
 #pragma unroll
             for (int c = 0; c < NCH; ++c) {
-                const V x = __builtin_nontemporal_load(
-                    reinterpret_cast<const V *>(slot + (int64_t)(row0 + r) * D + (c * LPR + p) * VEC));
+                const V x = load_tile_vec<V>(srs, tile_off(r, c));
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) s[r][c * VEC + e] = x[e];
             }
@@ -194,12 +196,12 @@ fused_kernel(StepArgs a, FrontArgs f) {
                 sumsq = fmaf(o, o, sumsq);
                 if (r == p) o_mine = o;
                 V x;
+                const __amdgpu_buffer_rsrc_t srs = tile_rsrc(slot, D * D * (int)sizeof(float));
 #pragma unroll
                 for (int c = 0; c < NCH; ++c) {
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) x[e] = alpha * s[r][c * VEC + e] + coef * kk[c * VEC + e];
-                    __builtin_nontemporal_store(
-                        x, reinterpret_cast<V *>(slot + (int64_t)(row0 + r) * D + (c * LPR + p) * VEC));
+                    store_tile_vec<V>(srs, tile_off(r, c), x);
                 }
             }
         }
@@ -259,14 +261,16 @@ fused_split_kernel(StepArgs a, FrontArgs f, float *ring_out) {
     const bool active = grp < TL::NGA;
     const int row0 = grp * RPL;
     float *slot = static_cast<float *>(a.state) + (int64_t)b * a.pitch + (int64_t)h * (D * D);
+    // the tile's vectors through a buffer descriptor with the decode's cache policy
+    const __amdgpu_buffer_rsrc_t srs = tile_rsrc(slot, D * D * (int)sizeof(float));
+    auto tile_off = [&](int r, int c) { return ((row0 + r) * D + (c * LPR + p) * VEC) * (int)sizeof(float); };
     float s[RPL][C];
     auto load_tile = [&]() {
 #pragma unroll
         for (int r = 0; r < RPL; ++r)
 #pragma unroll
             for (int c = 0; c < NCH; ++c) {
-                const V x = __builtin_nontemporal_load(
-                    reinterpret_cast<const V *>(slot + (int64_t)(row0 + r) * D + (c * LPR + p) * VEC));
+                const V x = load_tile_vec<V>(srs, tile_off(r, c));
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) s[r][c * VEC + e] = x[e];
             }
@@ -392,8 +396,7 @@ fused_split_kernel(StepArgs a, FrontArgs f, float *ring_out) {
             for (int cc = 0; cc < NCH; ++cc) {
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) x[e] = alpha * s[r][cc * VEC + e] + coef * kk[cc * VEC + e];
-                __builtin_nontemporal_store(
-                    x, reinterpret_cast<V *>(slot + (int64_t)(row0 + r) * D + (cc * LPR + p) * VEC));
+                store_tile_vec<V>(srs, tile_off(r, cc), x);
             }
         }
     }

@@ -63,11 +63,11 @@ __device__ __forceinline__ V load_tile_vec(__amdgpu_buffer_rsrc_t r, int byte_of
     static_assert(sizeof(V) == 16, "16-byte vectors");
     return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kTileLoadPolicy));
 }
-template <typename V>
+template <typename V, int POLICY = kTileStorePolicy>
 __device__ __forceinline__ void store_tile_vec(__amdgpu_buffer_rsrc_t r, int byte_off, const V &x) {
     static_assert(sizeof(V) == 16, "16-byte vectors");
     typedef unsigned U __attribute__((ext_vector_type(4)));
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(U, x), r, byte_off, 0, kTileStorePolicy);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(U, x), r, byte_off, 0, POLICY);
 }
 
 // Non-temporal store of a state vector (8 or 16 bytes).  The vector goes out as
