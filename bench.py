@@ -13,9 +13,9 @@ Prints ONE JSON line.  ``value`` is state GB/s (2*B*NV*D*D*4 bytes per step /
 step time); ``roofline`` covers the decode kernel with its full algorithmic
 bytes (state + inputs + outputs) against the 8 TB/s HBM peak; ``cpu_baseline``
 times the CPU oracle on a bounded sample of the same workload.  ``extra`` holds
-the other workloads (binary16 state at B=256, the 4096-token sequence
-recurrence, the B=1 real-head token over 48 layers, the cache-resident B=64
-case).
+the other workloads (binary16 state at B=256, the fused-norm decode at other
+batch sizes, the 4096-token sequence recurrence, the B=1 real-head token over
+48 layers, the cache-resident B=64 case).
 """
 from __future__ import annotations
 
@@ -325,6 +325,58 @@ def run_norm_q(g, calls: int, pools: int = 16):
             "ms_per_call": round(ms, 5),
             "state_GBps": round(2.0 * B * NV * D * D * 4 / ms / 1e6, 1),
             "hbm_frac_algorithmic": round(algo / ms / 1e6 / HBM_PEAK_GBS, 4)}
+
+
+def run_batches(g, batches=(16, 32, 48, 96, 128)):
+    """The fused-norm decode at other batch sizes, fp32 state (fp32 y) and
+    binary16 state (bf16 y), each on its own seeded case of the batched
+    workload's shape (padded pitch), rotated over enough pools to stream from
+    HBM: median of 5 trials of 200 calls per point."""
+    import torch
+    from gated_deltanet_decode_delta_amd import inputs
+
+    dev = "cuda:0"
+    rows = []
+    for B in batches:
+        c = inputs.config_case("batched", B=B)
+        NK, NV, D = c.NK, c.NV, c.D
+        pools = max(4, min(48, -(-(3 << 29) // c.state.nbytes)))   # >= 1.5 GB in rotation
+        log(f"[bench] batch sweep: B={B} pools={pools}")
+        st0 = torch.from_numpy(c.state).to(dev)
+        states = [st0.clone() for _ in range(pools)]
+        st16 = [g.gdn_state_f32_to_f16(s) for s in states]
+        del st0
+        base = {n: torch.from_numpy(getattr(c, n)).to(dev) for n in ("q", "k", "v", "z", "alpha", "beta")}
+        sets = [{n: torch.roll(t, p, dims=0).contiguous() for n, t in base.items()} for p in range(pools)]
+        del base
+        gn = torch.from_numpy(c.gn).to(dev)
+        out = torch.empty((B, NV * D), dtype=torch.float32, device=dev)
+        ob = torch.empty((B, NV * D), dtype=torch.bfloat16, device=dev)
+
+        def f32(i):
+            p = i % pools
+            s = sets[p]
+            g.gdn_decode_norm(states[p], s["q"], s["k"], s["v"], s["alpha"], s["beta"], s["z"], gn,
+                              c.eps, out=out, num_k_heads=NK, num_v_heads=NV)
+
+        def f16(i):
+            p = i % pools
+            s = sets[p]
+            g.gdn_decode_f16state(st16[p], s["q"], s["k"], s["v"], s["alpha"], s["beta"], s["z"], gn,
+                                  c.eps, out=ob, num_k_heads=NK, num_v_heads=NV)
+
+        row = {"B": B, "pools": pools}
+        for name, fn, sb in (("f32", f32, 4), ("f16_state", f16, 2)):
+            ms = sorted(_timed(fn, 200, 10) for _ in range(5))[2]
+            algo = B * NV * head_bytes(D, NV, NK, sb, 4 if sb == 4 else 2, True)
+            row[name + "_us_per_call"] = round(ms * 1e3, 2)
+            row[name + "_hbm_frac_algorithmic"] = round(algo / ms / 1e6 / HBM_PEAK_GBS, 4)
+        rows.append(row)
+        del states, st16, sets, out, ob
+        torch.cuda.empty_cache()
+    return {"workload": "fused-norm decode by batch size: NV=48, NK=16, D=128, padded pool; fp32 "
+                        "state with fp32 y, and binary16 state with bf16 y",
+            "trials": "median of 5 trials x 200 calls per point", "points": rows}
 
 
 def run_raw(g, pools: int = 48):
@@ -907,8 +959,8 @@ def main():
     ap.add_argument("--pools", type=int, default=48)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-extra", action="store_true", help="main workload only")
-    ap.add_argument("--extras", default="raw,fp16_state,sequence,verify,norm_q,strided,fused,real_head",
-                    help="comma list of extra workloads: raw, fp16_state, sequence, verify, norm_q, "
+    ap.add_argument("--extras", default="raw,fp16_state,batches,sequence,verify,norm_q,strided,fused,real_head",
+                    help="comma list of extra workloads: raw, fp16_state, batches, sequence, verify, norm_q, "
                          "strided, fused, real_head")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--seq-only", action="store_true", help="time the sequence workload alone")
@@ -954,7 +1006,8 @@ def main():
                          "median_hbm_frac_algorithmic": round(
                              m["algo_bytes"] / m["trials"][2] / 1e6 / HBM_PEAK_GBS, 4)}}
     wanted = [] if args.no_extra else [w for w in args.extras.split(",") if w]
-    runners = {"raw": lambda: run_raw(g), "fp16_state": lambda: run_fp16(g, 100), "sequence": lambda: run_seq(g, 100),
+    runners = {"raw": lambda: run_raw(g), "fp16_state": lambda: run_fp16(g, 100),
+               "batches": lambda: run_batches(g), "sequence": lambda: run_seq(g, 100),
                "verify": lambda: run_verify(g, 100), "norm_q": lambda: run_norm_q(g, 200),
                "strided": lambda: run_strided(g, 200), "fused": lambda: run_fused(g, 200),
                "real_head": lambda: run_real_head(g, 50)}
