@@ -13,9 +13,9 @@ Prints ONE JSON line.  ``value`` is state GB/s (2*B*NV*D*D*4 bytes per step /
 step time); ``roofline`` covers the decode kernel with its full algorithmic
 bytes (state + inputs + outputs) against the 8 TB/s HBM peak; ``cpu_baseline``
 times the CPU oracle on a bounded sample of the same workload.  ``extra`` holds
-the other workloads (binary16 state at B=256, the fused-norm decode at other
-batch sizes, the 4096-token sequence recurrence, the B=1 real-head token over
-48 layers, the cache-resident B=64 case).
+the other workloads (binary16 state at B=256, the 4096-token sequence
+recurrence, the B=1 real-head token over 48 layers, the cache-resident B=64
+case); ``--extras batches`` adds the fused-norm decode at other batch sizes.
 """
 from __future__ import annotations
 
@@ -959,9 +959,11 @@ def main():
     ap.add_argument("--pools", type=int, default=48)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-extra", action="store_true", help="main workload only")
-    ap.add_argument("--extras", default="raw,fp16_state,batches,sequence,verify,norm_q,strided,fused,real_head",
-                    help="comma list of extra workloads: raw, fp16_state, batches, sequence, verify, norm_q, "
-                         "strided, fused, real_head")
+    ap.add_argument("--extras", default="raw,fp16_state,sequence,verify,norm_q,strided,fused,real_head",
+                    help="comma list of extra workloads: raw, fp16_state, sequence, verify, norm_q, "
+                         "strided, fused, real_head; also batches (the fused-norm decode at other "
+                         "batch sizes, not in the default run, so that a kernel trace of the default "
+                         "run keeps one shape per decode kernel)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--seq-only", action="store_true", help="time the sequence workload alone")
     ap.add_argument("--pmc-summarize", metavar="DIR",
