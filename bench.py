@@ -511,12 +511,13 @@ def run_real_head(g, tokens: int):
     import torch
     from gated_deltanet_decode_delta_amd import inputs
 
-    B, NK, NV, D, L = 1, 16, 48, 128, 48
+    cfg = inputs.CONFIGS["real_head"]
+    NK, NV, D, L = cfg["NK"], cfg["NV"], cfg["D"], cfg["layers"]
     dev = "cuda:0"
     log("[bench] real head: B=1, 48 layers")
     layers = []
     for l in range(L):
-        c = inputs.make_case(2000 + l, B=B, NK=NK, NV=NV, D=D)
+        c = inputs.real_head_layer(l)
         d = {n: torch.from_numpy(getattr(c, n)).to(dev) for n in ("q", "k", "v", "z", "alpha", "beta", "gn")}
         d["state"] = torch.from_numpy(c.state).to(dev)
         d["out"] = torch.empty((1, NV * D), device=dev)
@@ -527,7 +528,11 @@ def run_real_head(g, tokens: int):
             g.gdn_decode_norm(d["state"], d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["z"],
                               d["gn"], 1e-6, out=d["out"], num_k_heads=NK, num_v_heads=NV)
 
-    ms = _timed(token, tokens, 3)
+    # each figure: median of 5 trials of `tokens` tokens (48 calls each), warmup 10
+    def median5(fn):
+        return sorted(_timed(fn, tokens, 10) for _ in range(5))[2]
+
+    ms = median5(token)
     # the same 48 calls marshalled once (static buffers, as in a serving loop)
     calls = [g.prepare(g.gdn_decode_norm, d["state"], d["q"], d["k"], d["v"], d["alpha"], d["beta"],
                        d["z"], d["gn"], 1e-6, out=d["out"], num_k_heads=NK, num_v_heads=NV)
@@ -537,7 +542,7 @@ def run_real_head(g, tokens: int):
         for call in calls:
             call()
 
-    ms_prepared = _timed(token_prepared, tokens, 3)
+    ms_prepared = median5(token_prepared)
     del calls
     graph_ms = None
     try:
@@ -549,13 +554,14 @@ def run_real_head(g, tokens: int):
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             token(0)
-        graph_ms = _timed(lambda i: graph.replay(), tokens, 3)
+        graph_ms = median5(lambda i: graph.replay())
     except Exception as e:  # capture is an optional measurement
         log(f"[bench] graph capture skipped: {e}")
     state_bytes = 2.0 * L * NV * D * D * 4
     del layers
     torch.cuda.empty_cache()
     res = {"workload": "real head B=1, 48 layer states per token, fused norm fp32",
+           "trials": f"median of 5 trials x {tokens} tokens ({tokens * L} calls), warmup 10",
            "us_per_token": round(ms * 1e3, 2), "tokens_per_s": round(1e3 / ms, 1),
            "state_GBps": round(state_bytes / ms / 1e6, 1),
            "prepared_us_per_token": round(ms_prepared * 1e3, 2)}
@@ -1012,7 +1018,7 @@ def main():
                "batches": lambda: run_batches(g), "sequence": lambda: run_seq(g, 100),
                "verify": lambda: run_verify(g, 100), "norm_q": lambda: run_norm_q(g, 200),
                "strided": lambda: run_strided(g, 200), "fused": lambda: run_fused(g, 200),
-               "real_head": lambda: run_real_head(g, 50)}
+               "real_head": lambda: run_real_head(g, 100)}
     for w in wanted:
         extra[w] = runners[w]()
     cpu = None if args.no_cpu else cpu_baseline(args.cpu_seconds)

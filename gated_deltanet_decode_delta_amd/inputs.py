@@ -98,6 +98,16 @@ def config_case(name: str, **overrides) -> Case:
     return make_case(seed, **cfg)
 
 
+def real_head_layer(layer: int) -> Case:
+    """One of the real-head workload's 48 GDN layers, each with its own state
+    and inputs: layer ``l`` draws from seed 1000 * (the config's seed) + l."""
+    cfg = dict(CONFIGS["real_head"])
+    if not 0 <= layer < cfg.pop("layers"):
+        raise ValueError("layer out of range")
+    seed = cfg.pop("seed")
+    return make_case(1000 * seed + layer, **cfg)
+
+
 @dataclass
 class FrontCase:
     """Inputs of the decode with the fused input stage (conv ring, L2, gates)."""

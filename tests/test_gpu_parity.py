@@ -122,10 +122,11 @@ def test_tiny_config_all_paths(g):
 
 # --------------------------------------------------------------------------- 2
 def test_real_head_layers(g):
-    """Real head shape (B=1, NV=48, NK=16, D=128), fused norm fp32, several of
-    the 48 independent layer states, every head checked."""
-    for layer in range(4):
-        c = inputs.make_case(200 + layer, B=1, NK=16, NV=48, D=128)
+    """Real head shape (B=1, NV=48, NK=16, D=128), fused norm fp32: one token
+    over all 48 independent layer states (the timed workload's inputs), every
+    head of every layer checked."""
+    for layer in range(inputs.CONFIGS["real_head"]["layers"]):
+        c = inputs.real_head_layer(layer)
         say("real_head layer", layer)
         ref_state = c.state.copy()
         ref = orc.decode(ref_state, c.q, c.k, c.v, c.alpha, c.beta, B=1, NK=16, NV=48, Dk=128,
