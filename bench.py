@@ -163,7 +163,8 @@ def run_fp16(g, calls: int):
             "min_ms_per_call": round(trials[0], 5),
             "state_GBps": round(state_bytes / ms / 1e6, 1),
             "hbm_frac_algorithmic": round(algo / ms / 1e6 / HBM_PEAK_GBS, 4),
-            "tokens_per_s_batch": round(B / ms * 1e3, 1)}
+            "tokens_per_s_batch": round(B / ms * 1e3, 1),
+            "model_tokens_per_s_48_layers": round(B / (48 * ms) * 1e3, 1)}
 
 
 def _cold_calls(fn, trials: int, pause_s: float):
@@ -1044,6 +1045,9 @@ def main():
                                f"{m['pools']} state pools in rotation",
                    "global_batch": B, "seq_len": 1, "parallelism": "single GPU"},
         "tokens_per_s_batch": round(B / ms * 1e3, 1),
+        # the same rate per model token: one token of each sequence steps all 48
+        # GDN layer states of the model, one call per layer
+        "model_tokens_per_s_48_layers": round(B / (48 * ms) * 1e3, 1),
         "hbm_frac_state": round(value / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
