@@ -1,0 +1,135 @@
+"""The entry points replayed from a HIP graph.
+
+A serving loop captures a decode token once and replays it.  Here one graph
+holds a fused-norm decode per layer, a binary16-state decode, a draft verify
+and both D = 128 sequence entry points (with z: the chunked kernels and the
+norm pass).  It is replayed three times, with eager work of the program between
+the replays, and after every replay each output and each state must equal, bit
+for bit, the same calls made eagerly on copies of the same buffers: the graph
+runs the same kernels on the same inputs, and no call records a memset.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from gated_deltanet_decode_delta_amd import inputs
+from gpu_util import dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def g():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gated_deltanet_decode_delta_amd as gdn
+    gdn.lib()
+    return gdn
+
+
+def say(*a):
+    print("[case]", *a, file=sys.stderr, flush=True)
+
+
+def _buffers(g):
+    """Inputs (shared by both copies) and one set of the buffers the calls
+    write: states and outputs."""
+    import torch
+    NK, NV, D = 16, 48, 128
+    layers = [inputs.make_case(3100 + l, B=3, NK=NK, NV=NV, D=D) for l in range(3)]
+    f16 = inputs.make_case(3200, B=5, NK=NK, NV=NV, D=D)
+    ver = inputs.make_case(3300, B=2, NK=NK, NV=NV, D=D, T=3)
+    seq = inputs.make_case(3400, B=2, NK=NK, NV=NV, D=D, T=37)
+    names = ("q", "k", "v", "z", "alpha", "beta", "gn")
+    ins = {"layers": [{n: dev(getattr(c, n)) for n in names} for c in layers],
+           "f16": {n: dev(getattr(f16, n)) for n in names},
+           "ver": {n: dev(getattr(ver, n)) for n in names},
+           "seq": {n: dev(getattr(seq, n)) for n in names}}
+    need = g.gdn_seq_workspace_bytes(seq.B, seq.T, NV, D)
+
+    def fresh():
+        nan = float("nan")
+        return {
+            "layers": [dev(c.state) for c in layers],
+            "layer_out": [torch.full((3, NV * D), nan, device="cuda:0") for _ in layers],
+            "f16": g.gdn_state_f32_to_f16(dev(f16.state)),
+            "f16_out": torch.full((5, NV * D), nan, device="cuda:0").to(torch.bfloat16),
+            "ver": dev(ver.state),
+            "ver_inter": torch.full((2 * 2, NV * D * D), nan, device="cuda:0"),
+            "ver_out": torch.full((2 * 3, NV * D), nan, device="cuda:0"),
+            "seq": dev(seq.state),
+            "seq_out": torch.full((2 * 37, NV * D), nan, device="cuda:0"),
+            "seq_ws_state": dev(seq.state),
+            "seq_ws_out": torch.full((2 * 37, NV * D), nan, device="cuda:0"),
+            "ws": torch.empty(max(need, 16), dtype=torch.uint8, device="cuda:0"),
+        }
+    return ins, fresh, (NK, NV, D), seq.eps
+
+
+def _token(g, ins, w, dims, eps):
+    """Every call of one step, on the written buffers `w`."""
+    NK, NV, D = dims
+    for d, st, out in zip(ins["layers"], w["layers"], w["layer_out"]):
+        g.gdn_decode_norm(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["z"], d["gn"], eps,
+                          out=out, num_k_heads=NK, num_v_heads=NV)
+    d = ins["f16"]
+    g.gdn_decode_f16state(w["f16"], d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["z"], d["gn"],
+                          eps, out=w["f16_out"], num_k_heads=NK, num_v_heads=NV)
+    d = ins["ver"]
+    g.gdn_decode_verify(w["ver"], d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["z"], d["gn"],
+                        eps, out=w["ver_out"], inter_state=w["ver_inter"], num_tokens=3,
+                        num_k_heads=NK, num_v_heads=NV, head_dim=D)
+    d = ins["seq"]
+    g.gdn_recurrence_seq(w["seq"], d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["z"], d["gn"],
+                         eps, out=w["seq_out"], seq_len=37, num_k_heads=NK, num_v_heads=NV,
+                         head_dim=D)
+    g.gdn_recurrence_seq_ws(w["seq_ws_state"], d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                            d["z"], d["gn"], eps, out=w["seq_ws_out"], workspace=w["ws"],
+                            seq_len=37, num_k_heads=NK, num_v_heads=NV, head_dim=D)
+
+
+def _same(a, b, what):
+    x, y = host(a).view(np.uint8), host(b).view(np.uint8)
+    assert x.shape == y.shape and np.array_equal(x, y), what
+
+
+def _compare(gw, ew, rep):
+    for i, (a, b) in enumerate(zip(gw["layers"], ew["layers"])):
+        _same(a, b, f"replay {rep}: layer {i} state")
+    for i, (a, b) in enumerate(zip(gw["layer_out"], ew["layer_out"])):
+        _same(a, b, f"replay {rep}: layer {i} y")
+    for k in ("f16", "f16_out", "ver", "ver_inter", "ver_out", "seq", "seq_out", "seq_ws_state",
+              "seq_ws_out"):
+        _same(gw[k], ew[k], f"replay {rep}: {k}")
+
+
+def test_graph_replays_match_eager_calls(g):
+    import torch
+    ins, fresh, dims, eps = _buffers(g)
+    gw, ew = fresh(), fresh()          # graph's buffers, eager reference buffers
+    torch.cuda.synchronize()
+    # warm-up on a side stream (as torch asks before capture), mirrored eagerly
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        _token(g, ins, gw, dims, eps)
+    torch.cuda.current_stream().wait_stream(side)
+    _token(g, ins, ew, dims, eps)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        _token(g, ins, gw, dims, eps)   # recorded, not run
+    torch.cuda.synchronize()
+    _compare(gw, ew, "after capture")
+    for rep in range(3):
+        say("graph replay", rep)
+        graph.replay()
+        torch.cuda.synchronize()
+        # the program's own eager work between replays
+        _token(g, ins, ew, dims, eps)
+        scratch = torch.randn(1 << 20, device="cuda:0")
+        float(scratch.sum())
+        torch.cuda.synchronize()
+        _compare(gw, ew, rep)
