@@ -1,12 +1,14 @@
 """The entry points replayed from a HIP graph.
 
 A serving loop captures a decode token once and replays it.  Here one graph
-holds a fused-norm decode per layer, a binary16-state decode, a draft verify
-and both D = 128 sequence entry points (with z: the chunked kernels and the
-norm pass).  It is replayed three times, with eager work of the program between
-the replays, and after every replay each output and each state must equal, bit
-for bit, the same calls made eagerly on copies of the same buffers: the graph
-runs the same kernels on the same inputs, and no call records a memset.
+holds a fused-norm decode per layer, the int8-quantised epilogue, a
+binary16-state decode, a draft verify, the decode with the fused input stage in
+both ring modes and both D = 128 sequence entry points (with z: the chunked
+kernels and the norm pass).  It is replayed three times, with eager work of the
+program between the replays, and after every replay each output and each state
+must equal, bit for bit, the same calls made eagerly on copies of the same
+buffers: the graph runs the same kernels on the same inputs, and no call
+records a memset.
 """
 import sys
 
@@ -48,6 +50,8 @@ def _buffers(g):
            "ver": {n: dev(getattr(ver, n)) for n in names},
            "seq": {n: dev(getattr(seq, n)) for n in names}}
     need = g.gdn_seq_workspace_bytes(seq.B, seq.T, NV, D)
+    fr = inputs.make_frontend_case(3500, B=3, NK=NK, NV=NV, D=D, taps=4)
+    ins["front"] = {n: dev(getattr(fr, n)) for n in ("x", "w", "br", "ar", "dt", "rate", "z", "gn")}
 
     def fresh():
         nan = float("nan")
@@ -64,6 +68,16 @@ def _buffers(g):
             "seq_ws_state": dev(seq.state),
             "seq_ws_out": torch.full((2 * 37, NV * D), nan, device="cuda:0"),
             "ws": torch.empty(max(need, 16), dtype=torch.uint8, device="cuda:0"),
+            "q8_state": dev(layers[0].state),
+            "q8_codes": torch.zeros((3, NV * D), dtype=torch.int8, device="cuda:0"),
+            "q8_scales": torch.full((3, NV * D // 32), nan, device="cuda:0"),
+            "fr_state": dev(fr.state),
+            "fr_ring": dev(fr.ring),
+            "fr_out": torch.full((3, NV * D), nan, device="cuda:0"),
+            "fr2_state": dev(fr.state),
+            "fr2_ring_a": dev(fr.ring),
+            "fr2_ring_b": torch.full_like(dev(fr.ring), nan),
+            "fr2_out": torch.full((3, NV * D), nan, device="cuda:0"),
         }
     return ins, fresh, (NK, NV, D), seq.eps
 
@@ -74,6 +88,22 @@ def _token(g, ins, w, dims, eps):
     for d, st, out in zip(ins["layers"], w["layers"], w["layer_out"]):
         g.gdn_decode_norm(st, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["z"], d["gn"], eps,
                           out=out, num_k_heads=NK, num_v_heads=NV)
+    d = ins["layers"][0]
+    g.gdn_decode_norm_q(w["q8_state"], d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["z"],
+                        d["gn"], eps, codes=w["q8_codes"], scales=w["q8_scales"], write_y=False,
+                        num_k_heads=NK, num_v_heads=NV)
+    f = ins["front"]
+    g.gdn_decode_fused(w["fr_state"], w["fr_ring"], f["x"], f["w"], f["br"], f["ar"], f["dt"],
+                       f["rate"], f["z"], f["gn"], eps, 1e-6, out=w["fr_out"], num_k_heads=NK,
+                       num_v_heads=NV)
+    # two ring buffers: one step reads ring a and writes ring b, the next reads b
+    # and writes a, so each replay leaves the rings where the next one reads them
+    g.gdn_decode_fused(w["fr2_state"], w["fr2_ring_a"], f["x"], f["w"], f["br"], f["ar"], f["dt"],
+                       f["rate"], f["z"], f["gn"], eps, 1e-6, out=w["fr2_out"],
+                       conv_state_out=w["fr2_ring_b"], num_k_heads=NK, num_v_heads=NV)
+    g.gdn_decode_fused(w["fr2_state"], w["fr2_ring_b"], f["x"], f["w"], f["br"], f["ar"], f["dt"],
+                       f["rate"], f["z"], f["gn"], eps, 1e-6, out=w["fr2_out"],
+                       conv_state_out=w["fr2_ring_a"], num_k_heads=NK, num_v_heads=NV)
     d = ins["f16"]
     g.gdn_decode_f16state(w["f16"], d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["z"], d["gn"],
                           eps, out=w["f16_out"], num_k_heads=NK, num_v_heads=NV)
@@ -101,7 +131,8 @@ def _compare(gw, ew, rep):
     for i, (a, b) in enumerate(zip(gw["layer_out"], ew["layer_out"])):
         _same(a, b, f"replay {rep}: layer {i} y")
     for k in ("f16", "f16_out", "ver", "ver_inter", "ver_out", "seq", "seq_out", "seq_ws_state",
-              "seq_ws_out"):
+              "seq_ws_out", "q8_state", "q8_codes", "q8_scales", "fr_state", "fr_ring", "fr_out",
+              "fr2_state", "fr2_ring_a", "fr2_ring_b", "fr2_out"):
         _same(gw[k], ew[k], f"replay {rep}: {k}")
 
 
