@@ -64,5 +64,25 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+DEMO_SRC = os.path.join(os.path.dirname(HERE), "tests", "c", "gdn_c_demo.c")
+DEMO = DEMO_SRC[:-2]
+
+
+def build_c_demo() -> str:
+    """Compile the plain-C program that drives ``libgdn.so`` through ``gdn.h``
+    alone (hipMalloc buffers, no Python); it finds the library next to this
+    file and the HIP runtime under /opt/rocm by its run path."""
+    cc = os.environ.get("CC", "gcc")
+    cmd = [cc, "-std=c11", "-O2", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__", "-I", INCLUDE,
+           "-I", "/opt/rocm/include", DEMO_SRC, "-o", DEMO + ".tmp", "-L", HERE, "-lgdn",
+           "-L", "/opt/rocm/lib", "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../../gated_deltanet_decode_delta_amd", "-Wl,-rpath,/opt/rocm/lib"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"{cc} failed on {DEMO_SRC}:\n{res.stderr}")
+    os.replace(DEMO + ".tmp", DEMO)
+    return DEMO
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
